@@ -1,0 +1,459 @@
+"""Float64 CPU oracle for GPTQ layer quantization.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the CPU-baseline
+leg of the benchmark may import this module.  The product path (the HIP
+library and its Python binding) never imports, links or calls it, and it
+shares no code with that path.
+
+Written from the text of these pages (cited by title and section):
+
+* "GPTQ" (robocikowo.com, technologie-ai/gptq), sections "Jak dziala",
+  "Komponenty", "Hiperparametry", "Implementacja", "Zlozonosc obliczeniowa".
+* "Add gguf q4_k quantization" (pytorch/ao pull request 2001), its summary and
+  the review thread on super-block scales and separate scale/min tensors.
+* "GPTQ implementation with tensor subclasses" (pytorch/ao issue 577),
+  section "Background" (collect the layer's inputs, update its weight, use the
+  updated weight for the layer's outputs).
+* "Hugging Face AutoGPTQ and Transformers Integration", section
+  "The Quantization Algorithm" (one weight at a time, remaining weights
+  updated through the Hessian).
+
+The method is defined by an algorithm, not by a closed form, so the oracle
+takes its steps in the pages' order, plainly:
+
+1. H = 2 X X^T accumulated over token chunks ("Komponenty").
+2. Columns with H_ii = 0 carry no signal: H_ii := 1 and their weights are 0
+   (reading: the pages are silent on this).
+3. Act-order: columns processed by decreasing diag(H), the activation energy
+   ("Hiperparametry": order by activation importance); ties keep the lower
+   original index first.
+4. Damping: a value percdamp * mean(diag H) added to the diagonal
+   ("Hiperparametry": value added to the Hessian diagonal for stability).
+5. U = upper Cholesky factor of the inverse of the damped H, so U^T U = H^-1
+   ("Komponenty": Cholesky decomposition of the inverse Hessian).
+6. Column-by-column quantization in that fixed order; after each column the
+   not-yet-quantized columns absorb the error through the inverse Hessian
+   (Optimal Brain Surgeon rule, "Jak dziala" / "Komponenty").  Group grid
+   parameters are chosen at each group's first column from the then-current,
+   compensated weights ("Jak dziala": a scale per group).
+7. The blocked ("lazy") form of step 6, which reaches the same result
+   ("Komponenty": block updates).
+
+Precision: every float computation is float64, except the grid decisions
+(scale, zero point, code), which are taken in float32 -- the precision in
+which the GPU kernels take them -- so that both sides decide integers in the
+same precision; the compensation itself stays float64.  Rounding is
+round-half-to-even throughout (np.rint, and numpy's float16 conversion).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+f32 = np.float32
+
+
+class NotSPD(ArithmeticError):
+    """The damped Hessian is not symmetric positive definite."""
+
+
+# --------------------------------------------------------------------------
+# Step 1. Hessian of the layer inputs ("GPTQ", section "Komponenty").
+# --------------------------------------------------------------------------
+def hessian(chunks) -> np.ndarray:
+    """H = 2 * sum_c X_c X_c^T over token chunks X_c (d x n_c), in float64.
+
+    The matrix is the unnormalized 2 X X^T of the page; no averaging over
+    tokens (the result of the whole method is invariant to a positive scale
+    of H, see the pins)."""
+    G = None
+    for Xc in chunks:
+        Xc = np.asarray(Xc, dtype=np.float64)
+        P = Xc @ Xc.T
+        G = P if G is None else G + P
+    return 2.0 * G
+
+
+def hessian_diag(chunks) -> np.ndarray:
+    """diag(H) = 2 * sum_t x_it^2, the activation energy of each feature."""
+    s = None
+    for Xc in chunks:
+        Xc = np.asarray(Xc, dtype=np.float64)
+        p = np.einsum("it,it->i", Xc, Xc)
+        s = p if s is None else s + p
+    return 2.0 * s
+
+
+# --------------------------------------------------------------------------
+# Steps 2-4. Dead columns, act-order, damping ("Hiperparametry").
+# --------------------------------------------------------------------------
+def dead_columns(diag: np.ndarray) -> np.ndarray:
+    return np.asarray(diag) == 0
+
+
+def act_order_perm(diag: np.ndarray) -> np.ndarray:
+    """Processing order: decreasing activation energy, stable on ties."""
+    return np.argsort(-np.asarray(diag, dtype=np.float64), kind="stable")
+
+
+def damped_processing_hessian(H: np.ndarray, diag: np.ndarray, perm: np.ndarray,
+                              percdamp: float) -> np.ndarray:
+    """H_p = P (H with dead fix) P^T + delta I, delta = percdamp * mean(diag).
+
+    ``diag`` is the activation energy (diag of H) used for the dead test, the
+    order and the damping base."""
+    H = np.array(H, dtype=np.float64)
+    dead = dead_columns(diag)
+    H[dead, dead] = 1.0
+    dg = np.array(diag, dtype=np.float64)
+    dg[dead] = 1.0
+    delta = percdamp * np.mean(dg)
+    Hp = H[np.ix_(perm, perm)]
+    Hp[np.diag_indices_from(Hp)] += delta
+    return Hp
+
+
+# --------------------------------------------------------------------------
+# Step 5. Cholesky factor of the inverse Hessian ("Komponenty").
+# --------------------------------------------------------------------------
+def inverse_cholesky_upper(Hp: np.ndarray) -> np.ndarray:
+    """U upper triangular, positive diagonal, U^T U = Hp^-1.
+
+    Literal route: invert, then take the Cholesky factor of the inverse.
+    Raises NotSPD when Hp is not positive definite."""
+    try:
+        np.linalg.cholesky(Hp)           # Hp itself must be SPD
+        Hinv = np.linalg.inv(Hp)
+        L = np.linalg.cholesky(Hinv)     # Hinv = L L^T, L lower
+    except np.linalg.LinAlgError as exc:
+        raise NotSPD(str(exc)) from exc
+    return np.triu(L.T)
+
+
+def inverse_cholesky_upper_ul(Hp: np.ndarray) -> np.ndarray:
+    """Same U by the reversed route: Hp = R R^T with R upper, U = R^-1.
+
+    R is the Cholesky factor of Hp taken from the last index backwards
+    (R = J chol(J Hp J) J, J the exchange matrix); U = R^-1 is then upper with
+    U^T U = (R R^T)^-1.  The upper Cholesky factor of Hp^-1 is unique, so this
+    equals the literal route."""
+    try:
+        Lr = np.linalg.cholesky(Hp[::-1, ::-1])
+    except np.linalg.LinAlgError as exc:
+        raise NotSPD(str(exc)) from exc
+    R = Lr[::-1, ::-1]
+    d = Hp.shape[0]
+    U = np.linalg.solve(R, np.eye(d))
+    return np.triu(U)
+
+
+# --------------------------------------------------------------------------
+# Grids.  Decisions in float32 (the kernel's precision), see module header.
+# --------------------------------------------------------------------------
+def affine_params(v: np.ndarray, bits: int):
+    """Asymmetric min-max grid of one group for each row.
+
+    v: (rows, g) current weights of the group.  The range always contains 0
+    so that the zero point is an integer code in [0, maxq]; an all-zero group
+    uses the range [-1, 1].  Returns float32 (scale, zero, zero before rounding)."""
+    maxq = f32(2 ** bits - 1)
+    v = np.asarray(v, dtype=f32)
+    xmin = np.minimum(v.min(axis=1), f32(0))
+    xmax = np.maximum(v.max(axis=1), f32(0))
+    flat = xmin == xmax
+    xmin = np.where(flat, f32(-1), xmin)
+    xmax = np.where(flat, f32(1), xmax)
+    s = (xmax - xmin) / maxq
+    zr = -xmin / s
+    z = np.clip(np.rint(zr), f32(0), maxq)
+    return s.astype(f32), z.astype(f32), zr.astype(f32)
+
+
+def affine_quantize(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int):
+    """Code and dequantized value of one column: q = clamp(rint(w/s)+z), w^ = s(q-z)."""
+    maxq = f32(2 ** bits - 1)
+    w = np.asarray(w, dtype=f32)
+    q = np.clip(np.rint(w / s) + z, f32(0), maxq)
+    return q.astype(f32), (s * (q - z)).astype(f32)
+
+
+Q4K_SUB = 32      # weights per sub-block (6-bit scale and min each)
+Q4K_SUPER = 256   # weights per super-block (fp16 super-scale and super-min)
+
+
+def q4k_params(v: np.ndarray):
+    """Two-level grid of one super-block of 256 weights for each row.
+
+    From "Add gguf q4_k quantization": w = q * block_scale + block_min with
+    6-bit sub-block scales and mins under a super-block scale, chosen by a
+    plain min-max rule rather than gguf's search.  Reading used here (the
+    page gives the form, not the constants' derivation):
+
+    per sub-block b of 32: mn = min(v_b, 0), mx = max(v_b, 0),
+        s_b = (mx - mn)/15, m_b = -mn (>= 0);
+    D  = fp16(max_b s_b / 63), Dm = fp16(max_b m_b / 63);
+    sc_b = clamp(rint(s_b / D), 1, 63) if s_b > 0 and D > 0 else 0;
+    mc_b = clamp(rint(m_b / Dm), 0, 63) if Dm > 0 else 0;
+    effective S_b = D sc_b, M_b = Dm mc_b.
+
+    Returns D, Dm (float16), sc, mc (uint8, (rows, 8)), S, M (float32, (rows, 8))."""
+    v = np.asarray(v, dtype=f32)
+    rows = v.shape[0]
+    vb = v.reshape(rows, Q4K_SUPER // Q4K_SUB, Q4K_SUB)
+    mn = np.minimum(vb.min(axis=2), f32(0))
+    mx = np.maximum(vb.max(axis=2), f32(0))
+    s_b = (mx - mn) / f32(15)
+    m_b = -mn
+    D = (s_b.max(axis=1) / f32(63)).astype(np.float16)
+    Dm = (m_b.max(axis=1) / f32(63)).astype(np.float16)
+    Df = D.astype(f32)[:, None]
+    Dmf = Dm.astype(f32)[:, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sc = np.where((s_b > 0) & (Df > 0), np.clip(np.rint(s_b / Df), 1, 63), 0)
+        mc = np.where(Dmf > 0, np.clip(np.rint(m_b / Dmf), 0, 63), 0)
+    sc = sc.astype(f32)
+    mc = mc.astype(f32)
+    S = (Df * sc).astype(f32)
+    M = (Dmf * mc).astype(f32)
+    return D, Dm, sc.astype(np.uint8), mc.astype(np.uint8), S, M
+
+
+def q4k_quantize(w: np.ndarray, S: np.ndarray, M: np.ndarray):
+    """q = clamp(rint((w + M)/S), 0, 15) (0 when S = 0), w^ = S q - M."""
+    w = np.asarray(w, dtype=f32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(S > 0, np.clip(np.rint((w + M) / S), 0, 15), 0).astype(f32)
+    return q, (S * q - M).astype(f32)
+
+
+# --------------------------------------------------------------------------
+# Step 6/7. The column sweep with OBS compensation.
+# --------------------------------------------------------------------------
+@dataclass
+class GridSpec:
+    grid: str = "affine"   # "affine" or "q4k"
+    bits: int = 4
+    group: int = 128       # affine: weights per scale; q4k: 256
+
+    @property
+    def span(self) -> int:
+        return Q4K_SUPER if self.grid == "q4k" else self.group
+
+
+@dataclass
+class SweepResult:
+    q: np.ndarray          # codes (rows, d), processing order, float (integer-valued)
+    what: np.ndarray       # dequantized weights (rows, d), processing order, float32
+    scale: np.ndarray      # affine: (rows, d/g); q4k: effective S_b (rows, d/32)
+    zero: np.ndarray       # affine: (rows, d/g); q4k: effective M_b (rows, d/32)
+    ratio: np.ndarray      # pre-rounding value of each code, float32 (rows, d)
+    zratio: np.ndarray     # affine: pre-rounding zero point (rows, d/g); q4k: s_b/D
+    mratio: np.ndarray     # q4k: m_b/Dm (rows, d/32); affine: unused
+    D: np.ndarray | None = None
+    Dm: np.ndarray | None = None
+    sc: np.ndarray | None = None
+    mc: np.ndarray | None = None
+
+
+class _GroupState:
+    """Grid parameters of the group (super-block) currently being quantized."""
+
+    def __init__(self, spec: GridSpec, rows: int, d: int):
+        self.spec = spec
+        ng = d // spec.span
+        if spec.grid == "affine":
+            self.scale = np.zeros((rows, ng), f32)
+            self.zero = np.zeros((rows, ng), f32)
+            self.zratio = np.zeros((rows, ng), f32)
+            self.mratio = np.zeros((rows, 0), f32)
+        else:
+            nsub = d // Q4K_SUB
+            self.scale = np.zeros((rows, nsub), f32)
+            self.zero = np.zeros((rows, nsub), f32)
+            self.zratio = np.zeros((rows, nsub), f32)
+            self.mratio = np.zeros((rows, nsub), f32)
+            self.D = np.zeros((rows, ng), np.float16)
+            self.Dm = np.zeros((rows, ng), np.float16)
+            self.sc = np.zeros((rows, nsub), np.uint8)
+            self.mc = np.zeros((rows, nsub), np.uint8)
+
+    def choose(self, j: int, v: np.ndarray):
+        """Choose the grid of the group starting at column j from current weights v."""
+        sp = self.spec
+        gi = j // sp.span
+        if sp.grid == "affine":
+            s, z, zr = affine_params(v, sp.bits)
+            self.scale[:, gi], self.zero[:, gi], self.zratio[:, gi] = s, z, zr
+        else:
+            D, Dm, sc, mc, S, M = q4k_params(v)
+            b0 = j // Q4K_SUB
+            nb = Q4K_SUPER // Q4K_SUB
+            self.D[:, gi], self.Dm[:, gi] = D, Dm
+            self.sc[:, b0:b0 + nb], self.mc[:, b0:b0 + nb] = sc, mc
+            self.scale[:, b0:b0 + nb], self.zero[:, b0:b0 + nb] = S, M
+            vb = np.asarray(v, f32).reshape(v.shape[0], nb, Q4K_SUB)
+            mn = np.minimum(vb.min(axis=2), f32(0))
+            mx = np.maximum(vb.max(axis=2), f32(0))
+            s_b = (mx - mn) / f32(15)
+            with np.errstate(divide="ignore", invalid="ignore"):
+                self.zratio[:, b0:b0 + nb] = s_b / D.astype(f32)[:, None]
+                self.mratio[:, b0:b0 + nb] = (-mn) / Dm.astype(f32)[:, None]
+
+    def quantize(self, j: int, w: np.ndarray):
+        sp = self.spec
+        if sp.grid == "affine":
+            gi = j // sp.group
+            s, z = self.scale[:, gi], self.zero[:, gi]
+            q, what = affine_quantize(w, s, z, sp.bits)
+            ratio = np.asarray(w, f32) / s
+        else:
+            b = j // Q4K_SUB
+            S, M = self.scale[:, b], self.zero[:, b]
+            q, what = q4k_quantize(w, S, M)
+            with np.errstate(divide="ignore", invalid="ignore"):
+                ratio = (np.asarray(w, f32) + M) / S
+        return q, what, ratio
+
+
+def _check_shapes(W, U, spec: GridSpec, block: int | None):
+    r, d = W.shape
+    if U.shape != (d, d):
+        raise ValueError("U must be d x d")
+    if d % spec.span:
+        raise ValueError("cols must be a multiple of the group size")
+    if block is not None and not (spec.span % block == 0 or block % spec.span == 0):
+        raise ValueError("group and block sizes must divide one another")
+
+
+def gptq_sweep(Wp: np.ndarray, U: np.ndarray, spec: GridSpec,
+               block: int | None = None) -> SweepResult:
+    """Quantize Wp (rows x d, processing order) column by column.
+
+    block=None is the plain definition: after column j every later column k
+    takes W[:, k] -= e_j U[j, k] at once, with e_j = (w_j - w^_j)/U[j, j].
+    block=B is the lazy blocked form: inside a block of B columns the update
+    reaches only the block's own later columns, and the accumulated errors
+    reach everything after the block in one product Err @ U[block, after]."""
+    _check_shapes(Wp, U, spec, block)
+    W = np.array(Wp, dtype=np.float64)
+    U = np.asarray(U, dtype=np.float64)
+    r, d = W.shape
+    Q = np.zeros((r, d), f32)
+    What = np.zeros((r, d), f32)
+    ratio = np.zeros((r, d), f32)
+    gs = _GroupState(spec, r, d)
+    B = d if block is None else block
+    for i1 in range(0, d, B):
+        i2 = min(i1 + B, d)
+        hi = d if block is None else i2          # reach of the eager update
+        Err = np.zeros((r, i2 - i1))
+        for j in range(i1, i2):
+            if j % spec.span == 0:
+                gs.choose(j, W[:, j:j + spec.span].astype(f32))
+            w = W[:, j]
+            q, what, rat = gs.quantize(j, w.astype(f32))
+            e = (w - what.astype(np.float64)) / U[j, j]
+            W[:, j + 1:hi] -= np.outer(e, U[j, j + 1:hi])
+            Err[:, j - i1] = e
+            Q[:, j], What[:, j], ratio[:, j] = q, what, rat
+            W[:, j] = what
+        if block is not None and i2 < d:
+            W[:, i2:] -= Err @ U[i1:i2, i2:]
+    res = SweepResult(q=Q, what=What, scale=gs.scale, zero=gs.zero, ratio=ratio,
+                      zratio=gs.zratio, mratio=gs.mratio)
+    if spec.grid == "q4k":
+        res.D, res.Dm, res.sc, res.mc = gs.D, gs.Dm, gs.sc, gs.mc
+    return res
+
+
+def rtn(Wp: np.ndarray, spec: GridSpec) -> SweepResult:
+    """Round-to-nearest on the same grid rule and grouping, no compensation."""
+    d = Wp.shape[1]
+    return gptq_sweep(Wp, np.eye(d), spec)   # U = I: every update is zero
+
+
+# --------------------------------------------------------------------------
+# Whole layer.
+# --------------------------------------------------------------------------
+@dataclass
+class LayerResult:
+    perm: np.ndarray       # processing position -> original column
+    dead: np.ndarray       # bool per original column
+    U: np.ndarray          # float64, processing order
+    sweep: SweepResult     # processing order
+    q: np.ndarray          # codes, original column order
+    what: np.ndarray       # dequantized weights, original column order
+    g_idx: np.ndarray      # group of each original column
+
+
+def quantize_layer(W: np.ndarray, H: np.ndarray, diag: np.ndarray, *, bits: int,
+                   group: int, block: int | None, act_order: bool,
+                   percdamp: float, grid: str = "affine", route: str = "literal",
+                   rows: np.ndarray | None = None) -> LayerResult:
+    """GPTQ on one linear layer (W rows x d, H d x d, diag = activation energy).
+
+    ``rows`` restricts the sweep to a subset of W's rows (rows are independent
+    given U); W is then only those rows."""
+    W = np.asarray(W, dtype=np.float64)
+    d = W.shape[1]
+    diag = np.asarray(diag, dtype=np.float64)
+    dead = dead_columns(diag)
+    perm = act_order_perm(diag) if act_order else np.arange(d)
+    Hp = damped_processing_hessian(H, diag, perm, percdamp)
+    U = inverse_cholesky_upper(Hp) if route == "literal" else inverse_cholesky_upper_ul(Hp)
+    Wd = W.copy()
+    Wd[:, dead] = 0.0
+    spec = GridSpec(grid=grid, bits=bits, group=(Q4K_SUPER if grid == "q4k" else group))
+    sw = gptq_sweep(Wd[:, perm], U, spec, block)
+    q = np.empty_like(sw.q)
+    what = np.empty_like(sw.what)
+    q[:, perm] = sw.q
+    what[:, perm] = sw.what
+    gsz = Q4K_SUB if grid == "q4k" else group
+    g_idx = np.empty(d, np.int64)
+    g_idx[perm] = np.arange(d) // gsz
+    return LayerResult(perm=perm, dead=dead, U=U, sweep=sw, q=q, what=what, g_idx=g_idx)
+
+
+def reconstruction_error(W: np.ndarray, What: np.ndarray, H: np.ndarray) -> float:
+    """||(W - W^) X||_F^2 = 1/2 tr(dW H dW^T) for H = 2 X X^T (undamped)."""
+    dW = np.asarray(W, np.float64) - np.asarray(What, np.float64)
+    return 0.5 * float(np.einsum("ij,jk,ik->", dW, H, dW))
+
+
+# --------------------------------------------------------------------------
+# Storage: codes as a bit stream ("Zlozonosc obliczeniowa": about 4.x bits per
+# weight once packed with the per-group parameters).
+# --------------------------------------------------------------------------
+def pack(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Rows of b-bit codes -> rows of uint32 words, least significant bit first.
+
+    Code k of a row occupies stream bits [k*b, (k+1)*b); stream bit t is bit
+    (t mod 32) of word t // 32."""
+    codes = np.asarray(codes, dtype=np.int64)
+    r, n = codes.shape
+    if (n * bits) % 32:
+        raise ValueError("cols*bits must be a multiple of 32")
+    if codes.min(initial=0) < 0 or codes.max(initial=0) >= (1 << bits):
+        raise ValueError("code out of range")
+    nw = n * bits // 32
+    out = np.zeros((r, nw), dtype=np.uint64)
+    for k in range(n):
+        for b in range(bits):
+            t = k * bits + b
+            bit = (codes[:, k] >> b) & 1
+            out[:, t // 32] |= (bit.astype(np.uint64) << np.uint64(t % 32))
+    return out.astype(np.uint32)
+
+
+def unpack(words: np.ndarray, bits: int, n: int) -> np.ndarray:
+    words = np.asarray(words, dtype=np.uint64)
+    r = words.shape[0]
+    out = np.zeros((r, n), dtype=np.int64)
+    for k in range(n):
+        for b in range(bits):
+            t = k * bits + b
+            bit = (words[:, t // 32] >> np.uint64(t % 32)) & np.uint64(1)
+            out[:, k] |= bit.astype(np.int64) << b
+    return out
