@@ -1,0 +1,210 @@
+/*
+ * gptq.h -- C ABI of the MI355X (gfx950) GPTQ layer-quantization library
+ * (libgptq_mi355x.so).
+ *
+ * One linear layer W (rows x cols, out x in) and its calibration inputs X
+ * (cols features x n tokens) go through four calls, in the order the method
+ * is stated on the pages:
+ *
+ *   1. gptq_hessian_accumulate -- collect the layer's inputs into H = 2 X X^T
+ *      ("GPTQ implementation with tensor subclasses", section Background:
+ *      track the activations reaching the linear; "GPTQ", section Komponenty:
+ *      the Hessian of the layer inputs).
+ *   2. gptq_prepare_hinv -- damping, activation order and the Cholesky factor
+ *      of the inverse Hessian ("GPTQ", sections Komponenty and
+ *      Hiperparametry).
+ *   3. gptq_quantize_layer -- column-by-column quantization with Optimal
+ *      Brain Surgeon error compensation and block updates, producing the
+ *      codes and the updated (dequantized) weight the layer goes on with
+ *      ("GPTQ", section Jak dziala; "GPTQ implementation with tensor
+ *      subclasses", section Background: use the updated weight).
+ *   4. gptq_pack -- b-bit codes to a bit stream ("GPTQ", section
+ *      Zlozonosc obliczeniowa: about 4.x bits per weight as stored).
+ *
+ * Conventions shared by every call:
+ *  - Every pointer except `params` and the profiling outputs is a DEVICE
+ *    pointer on the current HIP device, owned by the caller.  Buffers must
+ *    not overlap unless stated.  Matrices are row-major and contiguous
+ *    unless a leading dimension is given.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = legacy default
+ *    stream) and is asynchronous, except where stated.  The library keeps no
+ *    device state between calls; calls on different streams may run
+ *    concurrently as long as their buffers are distinct.
+ *  - The library never allocates device memory.  Scratch memory is the
+ *    caller's `ws` buffer of `ws_bytes` bytes, sized by
+ *    gptq_workspace_bytes() and 256-byte aligned.
+ *  - Errors are returned as gptq_status, never thrown.  All argument checks
+ *    run on the host before any launch; on GPTQ_ERR_INVALID_ARG or
+ *    GPTQ_ERR_WORKSPACE nothing has been enqueued and no output was written.
+ *    gptq_last_error() then gives a message (thread-local).  A failed launch
+ *    returns GPTQ_ERR_DEVICE; outputs are then undefined.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = 1, /* bad size, pointer, alignment or parameter      */
+  GPTQ_ERR_NOT_SPD = 2,     /* damped Hessian not positive definite          */
+  GPTQ_ERR_DEVICE = 3,      /* a HIP call or kernel launch failed            */
+  GPTQ_ERR_WORKSPACE = 4    /* ws NULL, misaligned or smaller than required  */
+} gptq_status;
+
+typedef enum { GPTQ_DT_F32 = 0, GPTQ_DT_BF16 = 1 } gptq_dtype;
+
+typedef enum {
+  GPTQ_GRID_AFFINE = 0, /* asymmetric min-max scale + integer zero per group  */
+  GPTQ_GRID_Q4K = 1     /* two-level: 6-bit sub-block scale/min (32 weights)
+                           under fp16 super-scale/super-min (256 weights)     */
+} gptq_grid;
+
+/* Hyper-parameters ("GPTQ", section Hiperparametry: target precision, weights
+ * per scale, activation order, value added to the Hessian diagonal). */
+typedef struct {
+  int32_t bits;      /* AFFINE: 2..8; Q4K: must be 4                           */
+  int32_t group;     /* AFFINE: weights per scale, divides cols (cols = one
+                        group per row); Q4K: must be 256                      */
+  int32_t block;     /* lazy-update block B, 1..128; group % B == 0 or
+                        B % group == 0                                        */
+  int32_t act_order; /* 0: original column order; 1: decreasing diag(H)      */
+  float percdamp;    /* damping = percdamp * mean(diag H), >= 0 (0.01 usual)   */
+  int32_t grid;      /* gptq_grid                                             */
+} gptq_params;
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *gptq_last_error(void);
+
+/* Bytes of `ws` needed by gptq_prepare_hinv (for cols) and by
+ * gptq_quantize_layer (for rows x cols) with these parameters; the larger of
+ * the two, so one buffer serves both calls.  Returns 0 on invalid arguments. */
+size_t gptq_workspace_bytes(int64_t rows, int64_t cols, const gptq_params *p);
+
+/*
+ * H += 2 * X * X^T and hdiag += 2 * sum_t X[i,t]^2.
+ *
+ * ("GPTQ", section Komponenty: the Hessian of a linear layer is 2 X X^T of
+ * its input activations; section Zlozonosc obliczeniowa: the cost grows with
+ * calibration tokens times d^2, so X arrives in token chunks and the sums
+ * are accumulated across calls.)
+ *
+ *  H      d x d float, row-major.  Only the upper triangle including the
+ *         diagonal (j >= i) is read and written; the strict lower triangle is
+ *         never touched.  Zero it before the first chunk.
+ *  hdiag  d doubles: the activation energy of each feature, accumulated in
+ *         float64 (the column order under act-order is decided on it).  Zero
+ *         it before the first chunk.
+ *  X      d rows (features) x n_tok tokens, row stride ld_x elements
+ *         (ld_x >= n_tok), dtype x_dtype (BF16 = raw bfloat16 bits, or
+ *         F32).  16-byte aligned, and ld_x a multiple of 8 (BF16) or 4 (F32).
+ *  n_tok  tokens in this chunk (0 is a no-op).
+ *
+ * Products of bf16 inputs are exact in float32; sums are float32 in H.
+ */
+gptq_status gptq_hessian_accumulate(float *H, double *hdiag, int64_t d,
+                                    const void *X, int32_t x_dtype,
+                                    int64_t n_tok, int64_t ld_x, void *stream);
+
+/*
+ * Damping, order and inverse-Hessian factor.
+ *
+ * ("GPTQ", section Komponenty: Cholesky decomposition of the inverse
+ * Hessian; section Hiperparametry: column order by activation importance
+ * and a value added to the diagonal; section Implementacja: inverting an
+ * ill-conditioned Hessian is unstable.)
+ *
+ *  H, hdiag  as left by gptq_hessian_accumulate; read only.
+ *  dead      out, d bytes: 1 where hdiag[i] == 0 (a feature that never fires;
+ *            its H_ii is taken as 1 and its weights as 0).
+ *  perm      out, d int32: perm[p] = original column processed at position p.
+ *            act_order: decreasing hdiag, ties by lower index; else identity.
+ *  U         out, d x d float, row-major, in processing order: the upper
+ *            triangular factor with positive diagonal and U^T U = Hp^-1,
+ *            Hp = P (H with dead fix) P^T + percdamp * mean(diag) * I.  The
+ *            strict lower triangle is written as 0.
+ *  ws        scratch, >= gptq_workspace_bytes(., d, p).
+ *
+ * Synchronizes `stream` once at the end to read the positive-definiteness
+ * flag: GPTQ_ERR_NOT_SPD when a Cholesky pivot is <= 0 or not finite (U is
+ * then undefined; the caller may retry with a larger percdamp).
+ */
+gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d,
+                              const gptq_params *p, float *U, int32_t *perm,
+                              uint8_t *dead, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/*
+ * Quantize W column by column in processing order with OBS compensation.
+ *
+ * ("GPTQ", section Jak dziala: columns in a fixed order, the not yet
+ * quantized weights corrected through the inverse Hessian after each
+ * column, block updates, a scale per group, 4- or 3-bit result; "Add gguf
+ * q4_k quantization", summary: the two-level grid w = q * block_scale +
+ * block_min with a super-block scale, by a simple min-max choice.)
+ *
+ *  W        in/out, rows x cols float, original column order.  On return it
+ *           holds the dequantized weights W^ (what the layer uses next).
+ *  U, perm, dead  from gptq_prepare_hinv with the same d and params.
+ *  q        out, rows x cols bytes, codes in original column order.
+ *  g_idx    out, cols int32: group of each original column (AFFINE:
+ *           processing position / group; Q4K: processing position / 32).
+ *  AFFINE (else pass NULL):
+ *   scale   out, rows x (cols/group) float, groups in processing order.
+ *   zero    out, rows x (cols/group) bytes, integer zero point in [0, 2^bits).
+ *           w^ = scale * (q - zero).
+ *  Q4K (else pass NULL):
+ *   q4k_super_scale, q4k_super_min  out, rows x (cols/256) fp16 bit patterns.
+ *   q4k_sub_scale, q4k_sub_min      out, rows x (cols/32) bytes in [0, 63].
+ *           w^ = (D * sc) * q - (Dm * mc).
+ *  ws       scratch, >= gptq_workspace_bytes(rows, cols, p).
+ */
+gptq_status gptq_quantize_layer(float *W, int64_t rows, int64_t cols,
+                                const float *U, const int32_t *perm,
+                                const uint8_t *dead, const gptq_params *p,
+                                uint8_t *q, int32_t *g_idx, float *scale,
+                                uint8_t *zero, uint16_t *q4k_super_scale,
+                                uint16_t *q4k_super_min, uint8_t *q4k_sub_scale,
+                                uint8_t *q4k_sub_min, void *ws, size_t ws_bytes,
+                                void *stream);
+
+/*
+ * Pack b-bit codes into a bit stream per row.
+ *
+ * ("GPTQ", sections Jak dziala and Zlozonosc obliczeniowa: 4- or 3-bit
+ * weights, about 4.x bits per weight as stored.)
+ *
+ *  codes   rows x cols bytes, every value < 2^bits (larger values are masked
+ *          to their low `bits` bits).
+ *  packed  out, rows x (cols*bits/32) uint32.  Least significant bit first:
+ *          code k of a row occupies stream bits [k*bits, (k+1)*bits), and
+ *          stream bit t is bit (t mod 32) of word t / 32.
+ *  bits 1..8; cols*bits must be a multiple of 32 (pack zero points of a
+ *  whole layer as one row of rows*groups codes when a row alone is not).
+ */
+gptq_status gptq_pack(const uint8_t *codes, int64_t rows, int64_t cols,
+                      int32_t bits, uint32_t *packed, void *stream);
+
+/*
+ * Per-kernel timing with HIP events (for measurement, off by default).
+ * When enabled, every kernel launch of the library is bracketed by a pair of
+ * events on its stream.  gptq_profile_query synchronizes those events and
+ * returns the number of launches and their summed duration for the kernel
+ * `name` (e.g. "hessian_syrk_bf16"); 0 launches if unknown.  reset drops all
+ * records.  Not thread-safe; use from one host thread.
+ */
+void gptq_profile_enable(int on);
+void gptq_profile_reset(void);
+gptq_status gptq_profile_query(const char *name, int64_t *launches,
+                               double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

@@ -1,0 +1,262 @@
+// fp32 GEMM engine on fp32 MFMA (v_mfma_f32_32x32x2f32).
+//
+//   C = alpha * A * op(B) + beta * C,  A row-major M x K,
+//   op(B) = B (row-major K x N) or B^T (B row-major N x K).
+//
+// Used for the dense parts of the inverse-Hessian factorization (triangular
+// solve against the diagonal block, trailing symmetric update, the products
+// of the recursive triangular inverse) and for the lazy trailing update of
+// the column sweep ("GPTQ", section Komponenty: block updates).
+//
+// Tiles are 128 x 128 with four 64 x 64 wave tiles; operands are staged in
+// LDS k-major ([k][m]) so that an MFMA operand read is 32 consecutive floats.
+// A grouped launch runs up to kMaxGemmGroup independent problems of one
+// shape class, each workgroup finding its problem by tile index.
+#include "common.h"
+
+namespace gptq {
+namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kT = 128;         // tile edge
+constexpr int kBK = 16;         // k per stage
+constexpr int kPitch = 132;     // LDS row pitch (floats) of a k-major stage
+constexpr int kThreads = 256;
+
+// Stage one operand tile (kT rows x kBK k, row-major in memory with leading
+// dimension ld) into registers: 512 float4 chunks, 2 per thread.  Elements
+// outside [0, rows) x [k0, kend) are zero.
+template <bool kVec>
+__device__ __forceinline__ void load_rows(const float *__restrict__ P, int64_t ld, int rows,
+                                          int r0, int k0, int kend, int tid, f32x4_t (&v)[2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + kThreads * i;
+    const int r = c >> 2, kc = (c & 3) * 4;
+    const int gr = r0 + r, gk = k0 + kc;
+    f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+    if (gr < rows) {
+      const float *p = P + int64_t(gr) * ld + gk;
+      if (kVec && gk + 4 <= kend) {
+        x = *reinterpret_cast<const f32x4_t *>(p);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (gk + e < kend) ? p[e] : 0.f;
+      }
+    }
+    v[i] = x;
+  }
+}
+
+// Transposing store of a row-major staged tile into k-major LDS.
+__device__ __forceinline__ void store_rows_kmajor(float *lds, int tid, const f32x4_t (&v)[2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + kThreads * i;
+    const int r = c >> 2, kc = (c & 3) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lds[(kc + e) * kPitch + r] = v[i][e];
+  }
+}
+
+// B in row-major K x N: a tile (kBK k-rows x kT cols) is already k-major.
+template <bool kVec>
+__device__ __forceinline__ void load_kmajor(const float *__restrict__ P, int64_t ld, int cols,
+                                            int c0, int k0, int kend, int tid, f32x4_t (&v)[2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + kThreads * i;
+    const int k = c >> 5, nc = (c & 31) * 4;
+    const int gk = k0 + k, gc = c0 + nc;
+    f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+    if (gk < kend) {
+      const float *p = P + int64_t(gk) * ld + gc;
+      if (kVec && gc + 4 <= cols) {
+        x = *reinterpret_cast<const f32x4_t *>(p);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (gc + e < cols) ? p[e] : 0.f;
+      }
+    }
+    v[i] = x;
+  }
+}
+
+__device__ __forceinline__ void store_kmajor(float *lds, int tid, const f32x4_t (&v)[2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + kThreads * i;
+    const int k = c >> 5, nc = (c & 31) * 4;
+    *reinterpret_cast<f32x4_t *>(lds + k * kPitch + nc) = v[i];
+  }
+}
+
+template <int kTransB, bool kVec>
+__global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmGroup g) {
+  // ---- find problem and tile
+  int tile = blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < g.count && tile >= g.p[pi + 1].tile_begin) ++pi;
+  const GemmProblem &P = g.p[pi];
+  tile -= P.tile_begin;
+  int tm, tn;
+  if (g.lower_out) {
+    // lower tiles only (tn <= tm), row-major over the triangle
+    tm = int((sqrtf(8.f * tile + 1.f) - 1.f) * 0.5f);
+    while ((tm + 1) * (tm + 2) / 2 <= tile) ++tm;
+    while (tm * (tm + 1) / 2 > tile) --tm;
+    tn = tile - tm * (tm + 1) / 2;
+  } else {
+    tm = tile / P.tiles_n;
+    tn = tile % P.tiles_n;
+  }
+  const int m0 = tm * kT, n0 = tn * kT;
+
+  int kbeg = 0, kend = P.K;
+  if (g.b_lower) kbeg = min(n0, P.K) & ~(kBK - 1);
+  if (g.a_lower) kend = min(P.K, m0 + kT);
+
+  __shared__ __align__(16) float As[2][kBK * kPitch];
+  __shared__ __align__(16) float Bs[2][kBK * kPitch];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int nsteps = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
+  f32x4_t ra[2], rb[2];
+  auto load = [&](int s) {
+    const int k0 = kbeg + s * kBK;
+    load_rows<kVec>(P.A, P.lda, P.M, m0, k0, kend, tid, ra);
+    if (kTransB)
+      load_rows<kVec>(P.B, P.ldb, P.N, n0, k0, kend, tid, rb);
+    else
+      load_kmajor<kVec>(P.B, P.ldb, P.N, n0, k0, kend, tid, rb);
+  };
+  auto store = [&](int buf) {
+    store_rows_kmajor(As[buf], tid, ra);
+    if (kTransB)
+      store_rows_kmajor(Bs[buf], tid, rb);
+    else
+      store_kmajor(Bs[buf], tid, rb);
+  };
+
+  if (nsteps > 0) {
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+      const int buf = s & 1;
+      if (s + 1 < nsteps) load(s + 1);
+      const float *A = As[buf];
+      const float *B = Bs[buf];
+#pragma unroll
+      for (int kk = 0; kk < kBK / 2; ++kk) {
+        const int k = kk * 2 + (lane >> 5);
+        float a[2], b[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) a[i] = A[k * kPitch + wm * 64 + i * 32 + (lane & 31)];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[j] = B[k * kPitch + wn * 64 + j * 32 + (lane & 31)];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+      if (s + 1 < nsteps) store(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue.  32x32 result layout: lane l, element v ->
+  //      row 8*(v/4) + 4*(l/32) + v%4, col l%32.
+  const float alpha = P.alpha, beta = P.beta;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int gc = n0 + wn * 64 + j * 32 + (lane & 31);
+      if (gc >= P.N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int gr = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (gr >= P.M) continue;
+        if (g.lower_out && gr < gc) continue;
+        float *c = P.C + int64_t(gr) * P.ldc + gc;
+        const float r = alpha * acc[i][j][v];
+        *c = (beta == 0.f) ? r : r + beta * *c;
+      }
+    }
+}
+
+bool vec_ok(const void *p, int64_t ld) {
+  return (reinterpret_cast<uintptr_t>(p) % 16) == 0 && (ld % 4) == 0;
+}
+
+}  // namespace
+
+gptq_status gemm_f32_grouped(const GemmGroup &g0, hipStream_t stream, const char *name) {
+  GemmGroup g = g0;
+  int total = 0;
+  bool vec = true;
+  int n = 0;
+  for (int i = 0; i < g0.count; ++i) {
+    const GemmProblem &p = g0.p[i];
+    if (p.M <= 0 || p.N <= 0) continue;  // empty problem: nothing to write
+    GemmProblem q = p;
+    const int tm = (int)cdiv(p.M, kT), tn = (int)cdiv(p.N, kT);
+    q.tiles_n = tn;
+    q.tile_begin = total;
+    total += g.lower_out ? tm * (tm + 1) / 2 : tm * tn;
+    vec = vec && vec_ok(p.A, p.lda) && vec_ok(p.B, p.ldb);
+    g.p[n++] = q;
+  }
+  g.count = n;
+  g.total_tiles = total;
+  if (n == 0) return GPTQ_OK;
+  dim3 grid(total), block(kThreads);
+  if (g.transB) {
+    if (vec) return launch(name, gemm_f32_kernel<1, true>, grid, block, 0, stream, g);
+    return launch(name, gemm_f32_kernel<1, false>, grid, block, 0, stream, g);
+  }
+  if (vec) return launch(name, gemm_f32_kernel<0, true>, grid, block, 0, stream, g);
+  return launch(name, gemm_f32_kernel<0, false>, grid, block, 0, stream, g);
+}
+
+gptq_status gemm_f32(const float *A, int64_t lda, const float *B, int64_t ldb, float *C,
+                     int64_t ldc, int M, int N, int K, float alpha, float beta, int transB,
+                     int lower_out, int a_lower, int b_lower, hipStream_t stream,
+                     const char *name) {
+  GemmGroup g{};
+  g.count = 1;
+  g.transB = transB;
+  g.lower_out = lower_out;
+  g.a_lower = a_lower;
+  g.b_lower = b_lower;
+  GemmProblem &p = g.p[0];
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.alpha = alpha;
+  p.beta = beta;
+  return gemm_f32_grouped(g, stream, name);
+}
+
+}  // namespace gptq

@@ -1,0 +1,297 @@
+// Hessian accumulation H += 2 X X^T ("GPTQ", section Komponenty) and the
+// float64 activation energy hdiag += 2 sum_t x_it^2.
+//
+// bf16 path: a SYRK on bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 accumulate.
+// Only the upper-triangle 256x256 tiles of H are computed.  Each tile is
+// owned by one workgroup that runs the whole token loop, so H is updated by
+// one read-modify-write per tile and the result is deterministic (no split-K
+// atomics).  X is d x n row-major (tokens contiguous), so both MFMA operands
+// are K-contiguous rows of X and no transpose is needed anywhere.
+#include "common.h"
+
+namespace gptq {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 256;       // H tile edge
+constexpr int kBK = 32;          // tokens per pipeline stage
+constexpr int kThreads = 512;    // 8 waves: 2 along rows x 4 along cols
+constexpr int kRowBytes = kBK * 2;                 // 64 B of one X row per stage
+constexpr int kPanelBytes = kTile * kRowBytes;     // 16 KB per operand per stage
+constexpr int kGroupRows = 4;    // tile-order band height (panel reuse in L2)
+
+// 16-byte chunk position inside a 64-byte LDS row, XOR-swizzled so that the
+// MFMA operand reads (32 rows, same chunk) spread over all LDS banks.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+template <bool kCheckK>
+__device__ __forceinline__ void load_panel(const uint16_t *__restrict__ X, int64_t ld, int64_t d,
+                                           int64_t n, int64_t row0, int64_t k0, int tid,
+                                           u32x4_t (&r)[2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + kThreads * i;
+    const int rr = c >> 2, kc = c & 3;
+    const int64_t gr = row0 + rr;
+    const int64_t gk = k0 + kc * 8;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (gr < d) {
+      const uint16_t *p = X + gr * ld + gk;
+      if (!kCheckK || gk + 8 <= n) {
+        v = *reinterpret_cast<const u32x4_t *>(p);
+      } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (gk + e < n) ? p[e] : 0u;
+        v[0] = h[0] | (h[1] << 16);
+        v[1] = h[2] | (h[3] << 16);
+        v[2] = h[4] | (h[5] << 16);
+        v[3] = h[6] | (h[7] << 16);
+      }
+    }
+    r[i] = v;
+  }
+}
+
+__device__ __forceinline__ void store_panel(uint8_t *lds, int tid, const u32x4_t (&r)[2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + kThreads * i;
+    const int rr = c >> 2, kc = c & 3;
+    *reinterpret_cast<u32x4_t *>(lds + rr * kRowBytes + ((kc ^ swz(rr)) << 4)) = r[i];
+  }
+}
+
+__device__ __forceinline__ bf16x8_t read_frag(const uint8_t *lds, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8_t *>(lds + row * kRowBytes + ((chunk ^ swz(row)) << 4));
+}
+
+// Upper-triangle tile t (in band order) -> (ti, tj), ti <= tj.  Tiles are
+// ordered band by band (kGroupRows tile-rows per band); inside a band by
+// column tj, then by row.  Consecutive tiles share X panels.
+__device__ __forceinline__ void tile_coords(int t, int nt, int &ti, int &tj) {
+  int b0 = 0;
+  while (true) {
+    const int h = min(kGroupRows, nt - b0);
+    // tiles in this band: for tj in [b0, nt): rows b0 .. min(b0+h-1, tj)
+    const int tri = h * (h + 1) / 2;            // tj in [b0, b0+h)
+    const int rect = h * (nt - b0 - h);          // tj in [b0+h, nt)
+    if (t < tri + rect) {
+      if (t < tri) {
+        // tj = b0 + c, rows b0..b0+c: c*(c+1)/2 <= t < (c+1)(c+2)/2
+        int c = 0;
+        while ((c + 1) * (c + 2) / 2 <= t) ++c;
+        tj = b0 + c;
+        ti = b0 + (t - c * (c + 1) / 2);
+      } else {
+        const int u = t - tri;
+        tj = b0 + h + u / h;
+        ti = b0 + u % h;
+      }
+      return;
+    }
+    t -= tri + rect;
+    b0 += h;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads)
+    syrk_bf16_kernel(float *__restrict__ H, const uint16_t *__restrict__ X, int64_t d, int64_t n,
+                     int64_t ld, int nt, int ntiles, int per_xcd) {
+  // XCD-aware mapping: workgroups are dealt round-robin to the 8 XCDs, so
+  // give each XCD a contiguous run of the tile order (shared panels stay in
+  // that XCD's L2).
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3;
+  if (slot >= per_xcd) return;
+  const int t = xcd * per_xcd + slot;
+  if (t >= ntiles) return;
+  int ti, tj;
+  tile_coords(t, nt, ti, tj);
+  const bool diag = ti == tj;
+  const int64_t I0 = int64_t(ti) * kTile, J0 = int64_t(tj) * kTile;
+
+  extern __shared__ __align__(16) uint8_t smem[];
+  // stage s: A panel at smem + 2s*P, B panel at smem + (2s+1)*P
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;   // wave tile: rows wm*128.., cols wn*64..
+  // On a diagonal tile the two lowest-left wave tiles lie strictly below the
+  // diagonal and are skipped.
+  const bool idle = diag && (wm * 128 > wn * 64 + 63);
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int64_t nfull = n / kBK;
+  const int64_t nsteps = (n + kBK - 1) / kBK;
+  u32x4_t ra[2], rb[2];
+
+  auto load = [&](int64_t ks) {
+    const int64_t k0 = ks * kBK;
+    if (ks < nfull) {
+      load_panel<false>(X, ld, d, n, I0, k0, tid, ra);
+      if (!diag) load_panel<false>(X, ld, d, n, J0, k0, tid, rb);
+    } else {
+      load_panel<true>(X, ld, d, n, I0, k0, tid, ra);
+      if (!diag) load_panel<true>(X, ld, d, n, J0, k0, tid, rb);
+    }
+  };
+  auto store = [&](int s) {
+    store_panel(smem + (2 * s) * kPanelBytes, tid, ra);
+    if (!diag) store_panel(smem + (2 * s + 1) * kPanelBytes, tid, rb);
+  };
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int64_t ks = 0; ks < nsteps; ++ks) {
+    const int s = int(ks & 1);
+    if (ks + 1 < nsteps) load(ks + 1);
+    if (!idle) {
+      const uint8_t *A = smem + (2 * s) * kPanelBytes;
+      const uint8_t *B = diag ? A : A + kPanelBytes;
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int chunk = kk * 2 + (lane >> 5);
+        bf16x8_t a[4], b[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = read_frag(A, wm * 128 + i * 32 + (lane & 31), chunk);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[j] = read_frag(B, wn * 64 + j * 32 + (lane & 31), chunk);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (ks + 1 < nsteps) store(s ^ 1);
+    __syncthreads();
+  }
+  if (idle) return;
+
+  // Epilogue: H[i][j] += 2 * acc for i <= j inside the matrix.  32x32 MFMA
+  // result layout: lane l, element v -> row 8*(v/4) + 4*(l/32) + v%4, col l%32.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t gc = J0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t gr = I0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (gr <= gc && gc < d) {
+          float *p = H + gr * d + gc;
+          *p = *p + 2.f * acc[i][j][v];
+        }
+      }
+    }
+}
+
+// fp32 inputs: plain LDS-tiled FMA SYRK on 64x64 upper tiles (fp32 products
+// are not exact in bf16, so this path keeps fp32 operands end to end).
+constexpr int kFT = 64;
+__global__ void __launch_bounds__(256)
+    syrk_f32_kernel(float *__restrict__ H, const float *__restrict__ X, int64_t d, int64_t n,
+                    int64_t ld) {
+  const int ti = blockIdx.y, tj = blockIdx.x;
+  if (ti > tj) return;
+  __shared__ float As[16][kFT + 1];
+  __shared__ float Bs[16][kFT + 1];
+  const int tid = threadIdx.x;
+  const int tr = tid / 16, tc = tid % 16;  // 4x4 outputs per thread
+  const int64_t I0 = int64_t(ti) * kFT, J0 = int64_t(tj) * kFT;
+  float acc[4][4] = {};
+  for (int64_t k0 = 0; k0 < n; k0 += 16) {
+    for (int e = tid; e < kFT * 16; e += 256) {
+      const int r = e / 16, k = e % 16;
+      const int64_t gk = k0 + k;
+      As[k][r] = (I0 + r < d && gk < n) ? X[(I0 + r) * ld + gk] : 0.f;
+      Bs[k][r] = (J0 + r < d && gk < n) ? X[(J0 + r) * ld + gk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] += As[k][tr * 4 + a] * Bs[k][tc * 4 + b];
+    __syncthreads();
+  }
+  for (int a = 0; a < 4; ++a)
+    for (int b = 0; b < 4; ++b) {
+      const int64_t gr = I0 + tr * 4 + a, gc = J0 + tc * 4 + b;
+      if (gr <= gc && gc < d) H[gr * d + gc] += 2.f * acc[a][b];
+    }
+}
+
+// hdiag[i] += 2 * sum_t x_it^2 in float64, one workgroup per feature row,
+// fixed reduction order (deterministic).
+template <typename T>
+__device__ __forceinline__ double to_f64(T v);
+template <>
+__device__ __forceinline__ double to_f64<uint16_t>(uint16_t v) {
+  return (double)__uint_as_float(uint32_t(v) << 16);
+}
+template <>
+__device__ __forceinline__ double to_f64<float>(float v) {
+  return (double)v;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+    diag_energy_kernel(double *__restrict__ hdiag, const T *__restrict__ X, int64_t n, int64_t ld) {
+  const int64_t row = blockIdx.x;
+  const T *x = X + row * ld;
+  double s = 0.0;
+  for (int64_t t = threadIdx.x; t < n; t += 256) {
+    const double v = to_f64<T>(x[t]);
+    s = fma(v, v, s);
+  }
+  __shared__ double red[256];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) hdiag[row] += 2.0 * red[0];
+}
+
+}  // namespace
+
+gptq_status hessian_accumulate_impl(float *H, double *hdiag, int64_t d, const void *X,
+                                    int x_dtype, int64_t n_tok, int64_t ld_x,
+                                    hipStream_t stream) {
+  if (x_dtype == GPTQ_DT_BF16) {
+    const uint16_t *Xb = static_cast<const uint16_t *>(X);
+    const int nt = (int)cdiv(d, kTile);
+    const int ntiles = nt * (nt + 1) / 2;
+    const int per_xcd = (int)cdiv(ntiles, 8);
+    const size_t lds = 4 * kPanelBytes;
+    GPTQ_TRY(launch("hessian_syrk_bf16", syrk_bf16_kernel, dim3(8 * per_xcd), dim3(kThreads),
+                    lds, stream, H, Xb, d, n_tok, ld_x, nt, ntiles, per_xcd));
+    GPTQ_TRY(launch("hessian_diag", diag_energy_kernel<uint16_t>, dim3((unsigned)d), dim3(256), 0,
+                    stream, hdiag, Xb, n_tok, ld_x));
+  } else {
+    const float *Xf = static_cast<const float *>(X);
+    const unsigned nt = (unsigned)cdiv(d, kFT);
+    GPTQ_TRY(launch("hessian_syrk_f32", syrk_f32_kernel, dim3(nt, nt), dim3(256), 0, stream, H,
+                    Xf, d, n_tok, ld_x));
+    GPTQ_TRY(launch("hessian_diag", diag_energy_kernel<float>, dim3((unsigned)d), dim3(256), 0,
+                    stream, hdiag, Xf, n_tok, ld_x));
+  }
+  return GPTQ_OK;
+}
+
+}  // namespace gptq

@@ -1,0 +1,336 @@
+// Damping, activation order and the Cholesky factor of the inverse Hessian
+// ("GPTQ", sections Komponenty and Hiperparametry).
+//
+// U (upper, U^T U = Hp^-1) is reached without forming Hp^-1:
+//   A  = J Hp J            (J the exchange matrix: reversed processing order)
+//   A  = L L^T             (blocked right-looking Cholesky, lower, in place)
+//   U  = J L^-1 J          (recursive triangular inverse, then a rotation)
+// since Hp = (J L J)(J L J)^T with J L J upper, and the upper Cholesky factor
+// of Hp^-1 is unique.  This costs d^3/3 + d^3/3 flops instead of the d^3 +
+// d^3/3 of an explicit inverse followed by a second factorization.
+//
+// Workspace layout: A (d x d float) | T (scratch of the inverse products) |
+// flag (int) and delta (double).
+#include <algorithm>
+#include <vector>
+
+#include "common.h"
+
+namespace gptq {
+namespace {
+
+constexpr int kNB = 128;          // diagonal block of the factorization
+constexpr int kLP = kNB + 1;      // LDS pitch of a diagonal block
+constexpr int kPotrfThreads = 512;
+
+struct Node {
+  int b0, bm, b1, height;
+};
+
+int build_tree(int b0, int b1, std::vector<Node> &out) {
+  if (b1 - b0 <= 1) return 0;
+  const int bm = (b0 + b1) / 2;
+  const int h = 1 + std::max(build_tree(b0, bm, out), build_tree(bm, b1, out));
+  out.push_back({b0, bm, b1, h});
+  return h;
+}
+
+int64_t ldT(int64_t m1) { return (m1 + 3) & ~int64_t(3); }
+
+// Largest sum over one tree height of the T = L21 * X11 scratch (floats).
+int64_t tree_scratch(int64_t d, std::vector<Node> *nodes_out, int *hmax_out) {
+  const int nb = (int)cdiv(d, kNB);
+  std::vector<Node> nodes;
+  const int hmax = build_tree(0, nb, nodes);
+  int64_t best = 0;
+  for (int h = 1; h <= hmax; ++h) {
+    int64_t s = 0;
+    for (const Node &n : nodes)
+      if (n.height == h) {
+        const int64_t r0 = int64_t(n.b0) * kNB, rm = int64_t(n.bm) * kNB;
+        const int64_t r1 = std::min<int64_t>(int64_t(n.b1) * kNB, d);
+        s += (r1 - rm) * ldT(rm - r0);
+      }
+    best = std::max(best, s);
+  }
+  if (nodes_out) *nodes_out = nodes;
+  if (hmax_out) *hmax_out = hmax;
+  return best;
+}
+
+// ---------------------------------------------------------------- kernels
+// dead flags, damping delta = percdamp * mean(diag with dead -> 1), flag := 0.
+__global__ void __launch_bounds__(1024)
+    diag_prep_kernel(const double *__restrict__ hdiag, int64_t d, double percdamp,
+                     uint8_t *__restrict__ dead, double *__restrict__ delta, int *__restrict__ flag) {
+  __shared__ double red[1024];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < d; i += 1024) {
+    const double v = hdiag[i];
+    const bool z = v == 0.0;
+    dead[i] = z ? 1 : 0;
+    s += z ? 1.0 : v;
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    *delta = percdamp * (red[0] / (double)d);
+    *flag = 0;
+  }
+}
+
+// perm[rank(i)] = i, rank by decreasing hdiag, ties by lower index (stable).
+__global__ void __launch_bounds__(256)
+    rank_perm_kernel(const double *__restrict__ hdiag, int64_t d, int act_order,
+                     int32_t *__restrict__ perm) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (!act_order) {
+    if (i < d) perm[i] = (int32_t)i;
+    return;
+  }
+  __shared__ double keys[256];
+  // NaN keys (only from non-finite inputs) are ordered as -inf so that the
+  // ranks always form a permutation.
+  auto key = [](double v) { return v == v ? v : -INFINITY; };
+  const double ki = i < d ? key(hdiag[i]) : 0.0;
+  int64_t rank = 0;
+  for (int64_t j0 = 0; j0 < d; j0 += 256) {
+    __syncthreads();
+    const int64_t j = j0 + threadIdx.x;
+    keys[threadIdx.x] = j < d ? key(hdiag[j]) : 0.0;
+    __syncthreads();
+    const int lim = (d - j0) < 256 ? (int)(d - j0) : 256;
+    for (int t = 0; t < lim; ++t) {
+      const double kj = keys[t];
+      const int64_t jj = j0 + t;
+      rank += (kj > ki) || (kj == ki && jj < i);
+    }
+  }
+  if (i < d) perm[rank] = (int32_t)i;
+}
+
+// A[a][b] = Hp[d-1-a][d-1-b] on and below the diagonal, 0 above, where
+// Hp[x][y] = H[perm[x]][perm[y]] (upper triangle of H read), dead diagonal
+// entries taken as 1, and delta added on the diagonal.
+__global__ void __launch_bounds__(256)
+    gather_reversed_kernel(const float *__restrict__ H, int64_t d, const int32_t *__restrict__ perm,
+                           const uint8_t *__restrict__ dead, const double *__restrict__ delta,
+                           float *__restrict__ A) {
+  const int64_t a0 = int64_t(blockIdx.y) * 64, b0 = int64_t(blockIdx.x) * 64;
+  __shared__ int32_t qa[64], qb[64];
+  if (threadIdx.x < 64) {
+    const int64_t a = a0 + threadIdx.x;
+    qa[threadIdx.x] = a < d ? min(max(perm[d - 1 - a], 0), (int32_t)(d - 1)) : 0;
+  } else if (threadIdx.x < 128) {
+    const int64_t b = b0 + threadIdx.x - 64;
+    qb[threadIdx.x - 64] = b < d ? min(max(perm[d - 1 - b], 0), (int32_t)(d - 1)) : 0;
+  }
+  __syncthreads();
+  const double dl = *delta;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int ra = e >> 6, cb = e & 63;
+    const int64_t a = a0 + ra, b = b0 + cb;
+    if (a >= d || b >= d) continue;
+    float v = 0.f;
+    if (a > b) {
+      const int64_t x = qa[ra], y = qb[cb];
+      v = x < y ? H[x * d + y] : H[y * d + x];
+    } else if (a == b) {
+      const int64_t x = qa[ra];
+      const double h = dead[x] ? 1.0 : (double)H[x * d + x];
+      v = (float)(h + dl);
+    }
+    A[a * d + b] = v;
+  }
+}
+
+// Factor the diagonal block A[k0:k0+m, k0:k0+m] = L11 L11^T in LDS and, in
+// the same column loop, invert L11 by forward elimination (X = L11^-1).
+// Writes X (lower) and zeros (upper) back over the block.  A pivot that is
+// not > 0 and finite sets *flag.
+__global__ void __launch_bounds__(kPotrfThreads)
+    potrf_inv_block_kernel(float *__restrict__ A, int64_t d, int64_t k0, int m,
+                           int *__restrict__ flag) {
+  extern __shared__ float sm[];
+  float *L = sm;               // kNB x kLP
+  float *X = sm + kNB * kLP;   // kNB x kLP
+  const int tid = threadIdx.x;
+  float *Ab = A + k0 * d + k0;
+  for (int e = tid; e < m * m; e += kPotrfThreads) {
+    const int i = e / m, j = e % m;
+    L[i * kLP + j] = j <= i ? Ab[int64_t(i) * d + j] : 0.f;
+    X[i * kLP + j] = i == j ? 1.f : 0.f;
+  }
+  __syncthreads();
+  bool bad = false;
+  for (int j = 0; j < m; ++j) {
+    const float piv = L[j * kLP + j];
+    const bool ok = piv > 0.f && piv <= 3.402823466e38f;
+    bad = bad || !ok;
+    const float ljj = ok ? sqrtf(piv) : 1.f;
+    __syncthreads();  // every thread has read the pivot
+    // column j of L, and row j of X scaled by 1/l_jj (X row j has entries in cols <= j)
+    for (int i = j + 1 + tid; i < m; i += kPotrfThreads) L[i * kLP + j] /= ljj;
+    for (int c = tid; c <= j; c += kPotrfThreads) X[j * kLP + c] /= ljj;
+    if (tid == 0) L[j * kLP + j] = ljj;
+    __syncthreads();
+    // trailing update of L (lower part of rows/cols > j) and elimination of
+    // X rows below j: X[i][c] -= L[i][j] * X[j][c] for c <= j.
+    const int rem = m - j - 1;
+    const int wide = j + 1;
+    for (int e = tid; e < rem * (rem + wide); e += kPotrfThreads) {
+      const int ii = e / (rem + wide), cc = e % (rem + wide);
+      const int i = j + 1 + ii;
+      const float lij = L[i * kLP + j];
+      if (cc < rem) {
+        const int k = j + 1 + cc;
+        if (k <= i) L[i * kLP + k] -= lij * L[k * kLP + j];
+      } else {
+        const int c = cc - rem;
+        X[i * kLP + c] -= lij * X[j * kLP + c];
+      }
+    }
+    __syncthreads();
+  }
+  if (bad && tid == 0) *flag = 1;
+  for (int e = tid; e < m * m; e += kPotrfThreads) {
+    const int i = e / m, j = e % m;
+    Ab[int64_t(i) * d + j] = j <= i ? X[i * kLP + j] : 0.f;
+  }
+}
+
+// U[i][j] = Linv[d-1-i][d-1-j] for j >= i, 0 below the diagonal.
+__global__ void __launch_bounds__(256)
+    rotate_upper_kernel(const float *__restrict__ Linv, int64_t d, float *__restrict__ U) {
+  for (int64_t i = blockIdx.y; i < d; i += gridDim.y)
+    for (int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x; j < d; j += int64_t(gridDim.x) * 256)
+      U[i * d + j] = j >= i ? Linv[(d - 1 - i) * d + (d - 1 - j)] : 0.f;
+}
+
+bool g_lds_set = false;
+
+}  // namespace
+
+size_t prepare_ws_bytes(int64_t d) {
+  const size_t a = align256(size_t(d) * size_t(d) * sizeof(float));
+  const size_t t = align256(size_t(tree_scratch(d, nullptr, nullptr)) * sizeof(float));
+  return a + t + 256;
+}
+
+gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
+                              const gptq_params &p, float *U, int32_t *perm, uint8_t *dead,
+                              void *ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws_bytes;
+  std::vector<Node> nodes;
+  int hmax = 0;
+  const int64_t tsz = tree_scratch(d, &nodes, &hmax);
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  float *A = reinterpret_cast<float *>(base);
+  float *T = reinterpret_cast<float *>(base + align256(size_t(d) * size_t(d) * 4));
+  uint8_t *tail = base + align256(size_t(d) * size_t(d) * 4) + align256(size_t(tsz) * 4);
+  int *flag = reinterpret_cast<int *>(tail);
+  double *delta = reinterpret_cast<double *>(tail + 8);
+
+  GPTQ_TRY(launch("prep_diag", diag_prep_kernel, dim3(1), dim3(1024), 0, stream, hdiag, d,
+                  (double)p.percdamp, dead, delta, flag));
+  GPTQ_TRY(launch("prep_rank_perm", rank_perm_kernel, dim3((unsigned)cdiv(d, 256)), dim3(256), 0,
+                  stream, hdiag, d, (int)p.act_order, perm));
+  const unsigned g64 = (unsigned)cdiv(d, 64);
+  GPTQ_TRY(launch("prep_gather", gather_reversed_kernel, dim3(g64, g64), dim3(256), 0, stream, H,
+                  d, (const int32_t *)perm, (const uint8_t *)dead, (const double *)delta, A));
+
+  // ---- blocked Cholesky A = L L^T; diagonal blocks end up holding L_ii^-1
+  const size_t lds = size_t(2) * kNB * kLP * sizeof(float);
+  if (!g_lds_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)potrf_inv_block_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess)
+      return fail(GPTQ_ERR_DEVICE, std::string("cannot raise LDS limit: ") + hipGetErrorString(e));
+    g_lds_set = true;
+  }
+  for (int64_t k0 = 0; k0 < d; k0 += kNB) {
+    const int m = (int)std::min<int64_t>(kNB, d - k0);
+    GPTQ_TRY(launch("chol_diag_block", potrf_inv_block_kernel, dim3(1), dim3(kPotrfThreads), lds,
+                    stream, A, d, k0, m, flag));
+    const int64_t r = d - k0 - m;
+    if (r <= 0) break;
+    float *A21 = A + (k0 + m) * d + k0;
+    // L21 = A21 * L11^-T   (in place: one column tile, each workgroup owns its rows)
+    GPTQ_TRY(gemm_f32(A21, d, A + k0 * d + k0, d, A21, d, (int)r, m, m, 1.f, 0.f, 1, 0, 0, 0,
+                      stream, "chol_trsm"));
+    // A22 -= L21 L21^T (lower triangle)
+    float *A22 = A + (k0 + m) * d + (k0 + m);
+    GPTQ_TRY(gemm_f32(A21, d, A21, d, A22, d, (int)r, (int)r, m, -1.f, 1.f, 1, 1, 0, 0, stream,
+                      "chol_syrk"));
+  }
+
+  // ---- recursive triangular inverse, bottom-up by tree height:
+  //   T = L21 X11 ; X21 = -X22 T   (X11, X22 already inverted)
+  for (int h = 1; h <= hmax; ++h) {
+    std::vector<Node> lv;
+    for (const Node &n : nodes)
+      if (n.height == h) lv.push_back(n);
+    for (size_t s = 0; s < lv.size(); s += kMaxGemmGroup) {
+      const size_t e = std::min(lv.size(), s + kMaxGemmGroup);
+      GemmGroup g1{}, g2{};
+      g1.transB = 0;
+      g1.b_lower = 1;
+      g2.transB = 0;
+      g2.a_lower = 1;
+      int64_t off = 0;
+      for (size_t k = s; k < e; ++k) {
+        const Node &n = lv[k];
+        const int64_t r0 = int64_t(n.b0) * kNB, rm = int64_t(n.bm) * kNB;
+        const int64_t r1 = std::min<int64_t>(int64_t(n.b1) * kNB, d);
+        const int m1 = (int)(rm - r0), m2 = (int)(r1 - rm);
+        float *Tn = T + off;
+        off += int64_t(m2) * ldT(m1);
+        GemmProblem &a = g1.p[g1.count++];
+        a.A = A + rm * d + r0;  // L21
+        a.lda = d;
+        a.B = A + r0 * d + r0;  // X11
+        a.ldb = d;
+        a.C = Tn;
+        a.ldc = ldT(m1);
+        a.M = m2;
+        a.N = m1;
+        a.K = m1;
+        a.alpha = 1.f;
+        a.beta = 0.f;
+        GemmProblem &b = g2.p[g2.count++];
+        b.A = A + rm * d + rm;  // X22
+        b.lda = d;
+        b.B = Tn;
+        b.ldb = ldT(m1);
+        b.C = A + rm * d + r0;  // X21 over L21
+        b.ldc = d;
+        b.M = m2;
+        b.N = m1;
+        b.K = m2;
+        b.alpha = -1.f;
+        b.beta = 0.f;
+      }
+      GPTQ_TRY(gemm_f32_grouped(g1, stream, "trtri_gemm"));
+      GPTQ_TRY(gemm_f32_grouped(g2, stream, "trtri_gemm"));
+    }
+  }
+
+  GPTQ_TRY(launch("prep_rotate", rotate_upper_kernel,
+                  dim3((unsigned)std::min<int64_t>(cdiv(d, 256), 64), (unsigned)std::min<int64_t>(d, 16384)),
+                  dim3(256), 0,
+                  stream, (const float *)A, d, U));
+
+  int host_flag = 0;
+  hipError_t e = hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess)
+    return fail(GPTQ_ERR_DEVICE, std::string("prepare_hinv: ") + hipGetErrorString(e));
+  if (host_flag) return fail(GPTQ_ERR_NOT_SPD, "damped Hessian is not positive definite");
+  return GPTQ_OK;
+}
+
+}  // namespace gptq

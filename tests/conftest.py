@@ -20,6 +20,10 @@ def gpu_available() -> bool:
         return False
 
 
-@pytest.fixture(scope="session")
-def has_gpu():
-    return gpu_available()
+def pytest_collection_modifyitems(config, items):
+    if gpu_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU on this machine")
+    for it in items:
+        if "gpu" in it.keywords:
+            it.add_marker(skip)

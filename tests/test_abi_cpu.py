@@ -1,0 +1,105 @@
+"""The C-ABI library loads and exports every declared entry point; host-side
+argument validation answers without touching a GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from post_weight_quantization_layer_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "gptq.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gptq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_workspace_bytes():
+    p = B.make_params(4, 128, 128, True, 0.01)
+    n = B.gptq_workspace_bytes(4096, 11008, p)
+    assert n >= 11008 * 11008 * 4            # the factorization's d x d buffer
+    assert n >= 4096 * 11008 * 5             # act-order working copy + codes
+    p2 = B.make_params(4, 128, 128, False, 0.01)
+    assert B.gptq_workspace_bytes(4096, 11008, p2) <= n
+    with pytest.raises(B.GptqError):
+        B.gptq_workspace_bytes(4096, 11008, B.make_params(4, 100, 128, False, 0.01))
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(bits=9), "bits"),
+    (dict(bits=1), "bits"),
+    (dict(block=0), "block"),
+    (dict(block=129), "block"),
+    (dict(group=96, block=64), "divide"),
+    (dict(act_order=2), "act_order"),
+    (dict(percdamp=-1.0), "percdamp"),
+    (dict(percdamp=float("nan")), "percdamp"),
+    (dict(grid=1, bits=3, group=256), "4-bit"),
+    (dict(grid=1, bits=4, group=128), "256"),
+    (dict(grid=7), "grid"),
+    (dict(group=96, block=32), "multiple of group"),
+])
+def test_quantize_rejects_bad_params(kw, msg):
+    base = dict(bits=4, group=128, block=128, act_order=0, percdamp=0.01, grid=0)
+    base.update(kw)
+    p = B.gptq_params(base["bits"], base["group"], base["block"], base["act_order"],
+                      base["percdamp"], base["grid"])
+    L = B.lib()
+    st = L.gptq_quantize_layer(FAKE, 64, 1024, FAKE, FAKE, FAKE, ctypes.byref(p), FAKE, FAKE,
+                               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == B.GPTQ_ERR_INVALID_ARG
+    assert msg in B.gptq_last_error()
+
+
+def test_hessian_rejects_bad_args():
+    L = B.lib()
+    assert L.gptq_hessian_accumulate(None, FAKE, 16, FAKE, 1, 8, 8, None) == B.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, FAKE, 5, 8, 8, None) == B.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, FAKE, 1, 8, 4, None) == B.GPTQ_ERR_INVALID_ARG
+    assert "ld_x" in B.gptq_last_error()
+    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, FAKE, 1, 12, 12, None) == B.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_hessian_accumulate(FAKE, FAKE, 0, FAKE, 1, 8, 8, None) == B.GPTQ_ERR_INVALID_ARG
+    misaligned = ctypes.c_void_p(0x10002)
+    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, misaligned, 1, 8, 8, None) == B.GPTQ_ERR_INVALID_ARG
+    # an empty chunk is a no-op and succeeds without touching anything
+    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, None, 1, 0, 0, None) == B.GPTQ_OK
+
+
+def test_prepare_rejects_bad_workspace():
+    L = B.lib()
+    p = B.make_params(4, 128, 128, True, 0.01)
+    st = L.gptq_prepare_hinv(FAKE, FAKE, 1024, ctypes.byref(p), FAKE, FAKE, FAKE, None, 0, None)
+    assert st == B.GPTQ_ERR_WORKSPACE
+    st = L.gptq_prepare_hinv(FAKE, FAKE, 1024, ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 10, None)
+    assert st == B.GPTQ_ERR_WORKSPACE and "too small" in B.gptq_last_error()
+    st = L.gptq_prepare_hinv(FAKE, FAKE, 1024, ctypes.byref(p), FAKE, FAKE, FAKE,
+                             ctypes.c_void_p(0x10010), 1 << 40, None)
+    assert st == B.GPTQ_ERR_WORKSPACE and "aligned" in B.gptq_last_error()
+
+
+def test_pack_rejects_bad_args():
+    L = B.lib()
+    assert L.gptq_pack(FAKE, 4, 10, 3, FAKE, None) == B.GPTQ_ERR_INVALID_ARG   # 30 bits
+    assert L.gptq_pack(FAKE, 4, 32, 9, FAKE, None) == B.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_pack(None, 4, 32, 4, FAKE, None) == B.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_pack(FAKE, 0, 32, 4, FAKE, None) == B.GPTQ_OK                # nothing to do
+
+
+def test_profile_query_unknown_kernel():
+    assert B.gptq_profile_query("no_such_kernel") == (0, 0.0)

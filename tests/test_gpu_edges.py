@@ -1,0 +1,106 @@
+"""Edge cases of the HIP path: pack, not-positive-definite detection, dead
+columns, determinism, empty and degenerate inputs."""
+import numpy as np
+import pytest
+
+import oracle as O
+from post_weight_quantization_layer_amd import inputs as I
+from tests.gpu_harness import gpu_layer, log, oracle_layer
+from tests.parity import assert_codes, classify_codes, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("bits,rows,cols", [(2, 3, 48), (3, 5, 96), (4, 7, 40), (5, 2, 32),
+                                            (6, 3, 16), (7, 4, 64), (8, 9, 12), (3, 1, 11008)])
+def test_pack_matches_oracle(bits, rows, cols):
+    import torch
+    from post_weight_quantization_layer_amd import binding as B
+    rng = np.random.Generator(np.random.Philox(key=bits * 1000 + cols))
+    codes = rng.integers(0, 2 ** bits, size=(rows, cols)).astype(np.uint8)
+    dev = torch.device("cuda")
+    c = torch.from_numpy(codes).to(dev)
+    out = torch.empty((rows, cols * bits // 32), dtype=torch.int32, device=dev)
+    B.gptq_pack(c, bits, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32)
+    np.testing.assert_array_equal(got, O.pack(codes, bits))
+
+
+def test_not_spd_is_reported():
+    import torch
+    from post_weight_quantization_layer_amd import binding as B
+    d = 300
+    dev = torch.device("cuda")
+    H = torch.zeros((d, d), dtype=torch.float32, device=dev)
+    idx = torch.arange(d, device=dev)
+    H[idx, idx] = 1.0
+    H[17, 17] = -5.0                        # indefinite, large enough to beat damping
+    hdiag = torch.ones(d, dtype=torch.float64, device=dev)
+    p = B.make_params(4, 100, 100, False, 0.0)
+    U = torch.empty_like(H)
+    perm = torch.empty(d, dtype=torch.int32, device=dev)
+    dead = torch.empty(d, dtype=torch.uint8, device=dev)
+    ws = torch.empty(B.gptq_workspace_bytes(8, d, p), dtype=torch.uint8, device=dev)
+    with pytest.raises(B.NotSPDError):
+        B.gptq_prepare_hinv(H, hdiag, p, U, perm, dead, ws)
+    with pytest.raises(O.NotSPD):
+        O.inverse_cholesky_upper(np.diag(np.where(np.arange(d) == 17, -5.0, 1.0)))
+    # the same buffers work again afterwards
+    H[17, 17] = 2.0
+    B.gptq_prepare_hinv(H, hdiag, p, U, perm, dead, ws)
+    torch.cuda.synchronize()
+    u = U.cpu().numpy()
+    expect = np.ones(d)
+    expect[17] = 1 / np.sqrt(2.0)
+    np.testing.assert_allclose(np.diag(u), expect, rtol=1e-6)
+    assert np.all(u - np.diag(np.diag(u)) == 0)
+
+
+def test_dead_column_and_diagonal_hessian():
+    """A zero feature row: dead column, zero weights, processed last.  With
+    disjoint feature supports H is diagonal and GPTQ equals round-to-nearest."""
+    cfg = I.CONFIGS["q_proj_4096x4096_int4_g128"].with_(rows=70, cols=256, tokens=1024,
+                                                       act_order=True)
+    W = I.weight(cfg)
+    X = np.zeros((256, 1024), np.float32)
+    for i in range(256):
+        if i != 37:
+            X[i, 4 * i: 4 * i + 4] = 1.0 + (i % 7) / 8.0
+    store = [I.bf16_bits(X)]
+    g = gpu_layer(cfg, W, store)
+    o, H, diag = oracle_layer(cfg, W.astype(np.float64), [X])
+    assert g.dead[37] and g.dead.sum() == 1
+    assert np.all(g.W_hat[:, 37] == 0)
+    np.testing.assert_array_equal(g.perm, o.perm)
+    np.testing.assert_array_equal(g.q, o.q)
+    np.testing.assert_array_equal(g.W_hat, o.what)
+    assert np.all(np.triu(g.U, 1) == 0)
+
+
+def test_bitwise_deterministic():
+    cfg = I.CONFIGS["down_proj_4096x11008_int4_g128_actorder"].with_(rows=96, cols=640,
+                                                                    tokens=1500)
+    W = I.weight(cfg)
+    store = [I.x_chunk_storage(cfg, 0, 1500)]
+    a = gpu_layer(cfg, W, store)
+    b = gpu_layer(cfg, W, store)
+    for f in ("H", "hdiag", "U", "q", "W_hat", "scale", "zero"):
+        np.testing.assert_array_equal(getattr(a, f), getattr(b, f), err_msg=f)
+
+
+@pytest.mark.parametrize("block,group", [(32, 128), (64, 64), (128, 32), (16, 256)])
+def test_block_group_combinations(block, group):
+    """Blocks smaller than, equal to and larger than the group give the
+    oracle's result (the method's result does not depend on B)."""
+    cfg = I.CONFIGS["up_proj_28672x8192_int3_g128_actorder"].with_(
+        rows=64, cols=512, tokens=1200, block=block, group=group)
+    W = I.weight(cfg)
+    store = [I.x_chunk_storage(cfg, 0, 1200)]
+    f32 = [I.bf16_to_f32(store[0])]
+    g = gpu_layer(cfg, W, store)
+    o, H, diag = oracle_layer(cfg, W.astype(np.float64), f32)
+    rep = classify_codes(g.q[:, o.perm], o.sweep, "affine", group)
+    log(f"[edges] B={block} g={group}: {rep.mismatches} code mismatches")
+    assert_codes(rep)
+    assert rel_fro(g.U, o.U) <= 1e-4
