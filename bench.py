@@ -1,0 +1,227 @@
+"""Benchmark: milliseconds per layer of GPTQ on one MI355X.
+
+One step = the whole hot path for one linear layer over its calibration
+batch: zero H, accumulate H over the token chunks, damping + act-order +
+inverse-Hessian factor, the quantization sweep with its trailing updates,
+and packing of codes and zero points.  Inputs (X in bf16, a pristine W per
+step) are resident in HBM before the timed region starts.
+
+Prints one JSON line.  Per-kernel times come from the library's own HIP
+events recorded on the launch stream (gptq_profile_*), over the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from post_weight_quantization_layer_amd import inputs as I  # noqa: E402
+
+METRIC = "ms per layer GPTQ (int4 g128, 4096×11008) + MFMA util of SYRK/GEMM"
+PEAK = {"bf16_mfma": 2500.0, "f32_mfma": 157.3, "hbm": 8000.0}   # TFLOP/s, GB/s
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_work(cfg, chunk):
+    """Algorithmic work of one launch of each main kernel.
+
+    hessian_syrk_bf16: d(d+1) n_c flops (upper triangle incl. diagonal, 2 per MAC);
+    trailing_gemm / chol_* / trtri_gemm: summed over the launches of one step."""
+    d, r, B = cfg.cols, cfg.rows, cfg.block
+    work = {"hessian_syrk_bf16": ("bf16_mfma", d * (d + 1) * chunk)}
+    # trailing update: sum over blocks of 2 r B (d - i2)
+    tr = sum(2 * r * min(B, d - i1) * (d - i1 - min(B, d - i1)) for i1 in range(0, d, B))
+    work["trailing_gemm"] = ("f32_mfma", tr)
+    return work
+
+
+def cpu_baseline(cfg, chunk_tokens):
+    """The float64 oracle, as it stands, on a bounded sample of the same
+    workload, scaled to milliseconds per layer with the cost model of the
+    pages (H linear in tokens, the inverse factor cubic in d, the sweep and
+    packing linear in rows)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    d, r = cfg.cols, cfg.rows
+    ntok = 1024
+    x = I.x_chunk(cfg, 0, ntok)
+    t0 = time.perf_counter()
+    H = O.hessian([x])
+    diag = O.hessian_diag([x])
+    t_h = (time.perf_counter() - t0) * (cfg.tokens / ntok)
+    ds = d // 4
+    t0 = time.perf_counter()
+    perm = O.act_order_perm(diag[:ds]) if cfg.act_order else np.arange(ds)
+    Hp = O.damped_processing_hessian(H[:ds, :ds], diag[:ds], perm, cfg.percdamp)
+    O.inverse_cholesky_upper(Hp)
+    t_u = (time.perf_counter() - t0) * (d / ds) ** 3
+    del H, Hp
+    nrow = 8
+    W = I.weight_rows(cfg, np.arange(nrow)).astype(np.float64)
+    U = np.eye(d)   # the sweep's cost does not depend on U's values
+    t0 = time.perf_counter()
+    sw = O.gptq_sweep(W, U, O.GridSpec(cfg.grid, cfg.bits, cfg.group))
+    t_s = (time.perf_counter() - t0) * (r / nrow)
+    t0 = time.perf_counter()
+    O.pack(sw.q.astype(np.int64), cfg.bits)
+    t_p = (time.perf_counter() - t0) * (r / nrow)
+    total_ms = (t_h + t_u + t_s + t_p) * 1e3
+    return {"value": round(total_ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
+            "sample": (f"H on {ntok} of {cfg.tokens} tokens (x{cfg.tokens // ntok}); damping, "
+                       f"act-order and inverse factor on the leading {ds}x{ds} block "
+                       f"(x(d/{ds})^3); sweep and pack over all {d} columns of {nrow} of {r} "
+                       f"rows (x{r // nrow}); float64 numpy/OpenBLAS"),
+            "split_ms": {"hessian": round(t_h * 1e3, 1), "inverse_factor": round(t_u * 1e3, 1),
+                         "sweep": round(t_s * 1e3, 1), "pack": round(t_p * 1e3, 1)}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default=I.HEADLINE, choices=sorted(I.CONFIGS))
+    ap.add_argument("--chunk-tokens", type=int, default=32768)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(a layer's rows would shard across GPUs with one broadcast of U); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from post_weight_quantization_layer_amd import binding as B
+    from post_weight_quantization_layer_amd.layer import GptqLayer
+
+    cfg = I.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+    chunk = min(args.chunk_tokens, cfg.tokens)
+    spans = I.token_chunks(cfg, chunk)
+
+    # ---- inputs resident in HBM
+    t0 = time.time()
+    xdt = torch.bfloat16 if cfg.x_dtype == "bf16" else torch.float32
+    X = torch.empty((cfg.cols, cfg.tokens), dtype=xdt, device=dev)
+    for (a, n) in I.token_chunks(cfg, 8192):
+        xs = I.x_chunk_storage(cfg, a, n)
+        src = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16) if xs.dtype == np.uint16 \
+            else torch.from_numpy(xs)
+        X[:, a:a + n].copy_(src)
+    W0 = torch.from_numpy(I.weight(cfg)).to(dev)
+    Ws = [torch.empty_like(W0) for _ in range(args.warmup + args.steps)]
+    for w in Ws:
+        w.copy_(W0)
+    layer = GptqLayer(cfg.rows, cfg.cols, bits=cfg.bits, group=cfg.group, block=cfg.block,
+                      act_order=cfg.act_order, percdamp=cfg.percdamp, grid=cfg.grid, device=dev)
+    out = layer.alloc_outputs()
+    packed_q = torch.empty((cfg.rows, cfg.cols * cfg.bits // 32), dtype=torch.int32, device=dev)
+    packed_z = None
+    if cfg.grid == "affine":
+        nz = out["zero"].numel()
+        packed_z = torch.empty(((nz * cfg.bits + 31) // 32,), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s: X {tuple(X.shape)} {X.dtype}, "
+        f"W {tuple(W0.shape)}, ws {layer.ws.numel() / 2**20:.0f} MiB")
+
+    def step(i):
+        layer.reset_hessian()
+        for (a, n) in spans:
+            B.gptq_hessian_accumulate(layer.H, layer.hdiag, X[:, a:a + n], n_tok=n,
+                                      ld_x=X.stride(0))
+        layer.prepare()
+        res = layer.quantize(Ws[i], out)
+        layer.pack_codes(res.q, packed_q)
+        if packed_z is not None and (out["zero"].numel() * cfg.bits) % 32 == 0:
+            layer.pack_zeros(out["zero"], packed_z)
+
+    for i in range(args.warmup):
+        step(i)
+        log(f"[bench] warmup step {i} done")
+    torch.cuda.synchronize()
+    if not args.no_profile:
+        B.gptq_profile_reset()
+        B.gptq_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    B.gptq_profile_enable(False)
+    ms = dt * 1e3 / args.steps
+    log(f"[bench] {args.steps} steps: {ms:.3f} ms/step")
+
+    kernels = {}
+    names = ["hessian_syrk_bf16", "hessian_syrk_f32", "hessian_diag", "prep_diag",
+             "prep_rank_perm", "prep_gather", "chol_diag_block", "chol_trsm", "chol_syrk",
+             "trtri_gemm", "prep_rotate", "quant_gather", "quant_zero_dead", "sweep_affine",
+             "sweep_q4k", "trailing_gemm", "quant_scatter", "quant_g_idx", "pack"]
+    if not args.no_profile:
+        for nme in names:
+            n, tms = B.gptq_profile_query(nme)
+            if n:
+                kernels[nme] = {"launches_per_step": n / args.steps,
+                                "ms_per_step": round(tms / args.steps, 4),
+                                "avg_us": round(tms / n * 1e3, 2)}
+    roof = None
+    if kernels:
+        work = kernel_work(cfg, chunk)
+        dom = max((k for k in kernels if k in work), key=lambda k: kernels[k]["ms_per_step"])
+        kind, flops_step = work[dom]
+        if dom == "hessian_syrk_bf16":
+            per_launch = flops_step
+        else:
+            per_launch = flops_step / kernels[dom]["launches_per_step"]
+        avg_s = kernels[dom]["avg_us"] * 1e-6
+        achieved = per_launch / avg_s / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": PEAK[kind], "unit": "TFLOP/s", "frac": round(achieved / PEAK[kind], 4),
+                "traffic": None, "algorithmic_flops_per_launch": per_launch}
+        for k in work:
+            if k in kernels:
+                kind_k, f = work[k]
+                pl = f if k == "hessian_syrk_bf16" else f / kernels[k]["launches_per_step"]
+                kernels[k]["tflops"] = round(pl / (kernels[k]["avg_us"] * 1e-6) / 1e12, 1)
+                kernels[k]["mfma_frac"] = round(kernels[k]["tflops"] / PEAK[kind_k], 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on a bounded sample ...")
+        cpu = cpu_baseline(cfg, chunk)
+        log(f"[bench] oracle: {cpu['value']} ms/layer on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC, "value": round(ms, 3), "unit": "ms", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": False, "scaling": "strong", "vs_baseline": None,
+        "dtype": "bf16+f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "rows": cfg.rows, "cols": cfg.cols,
+                   "tokens": cfg.tokens, "chunk_tokens": chunk, "bits": cfg.bits,
+                   "group": cfg.group, "block": cfg.block, "act_order": cfg.act_order,
+                   "grid": cfg.grid, "percdamp": cfg.percdamp},
+        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

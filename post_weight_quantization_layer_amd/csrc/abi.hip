@@ -95,7 +95,7 @@ void profile_end(ProfileToken tok, hipStream_t stream) {
   }
   (void)hipEventRecord(stop, stream);
   P.pending.push_back({tok.slot, tok.start, stop});
-  if (P.pending.size() > 4096) P.drain();
+  if (P.pending.size() > (size_t(1) << 18)) P.drain();
 }
 
 // ------------------------------------------------------------- validation

@@ -20,8 +20,6 @@ namespace gptq {
 namespace {
 
 constexpr int kNB = 128;          // diagonal block of the factorization
-constexpr int kLP = kNB + 1;      // LDS pitch of a diagonal block
-constexpr int kPotrfThreads = 512;
 
 struct Node {
   int b0, bm, b1, height;
@@ -148,58 +146,169 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// Factor the diagonal block A[k0:k0+m, k0:k0+m] = L11 L11^T in LDS and, in
-// the same column loop, invert L11 by forward elimination (X = L11^-1).
-// Writes X (lower) and zeros (upper) back over the block.  A pivot that is
-// not > 0 and finite sets *flag.
-__global__ void __launch_bounds__(kPotrfThreads)
+// ------------------------------------------------------ diagonal block
+// Factor the diagonal block A[k0:k0+m, k0:k0+m] = L11 L11^T and invert L11,
+// in LDS, with 32 x 32 leaves:
+//   for each leaf s (columns o = 32 s .. o + 31):
+//     one wavefront factors the leaf and inverts it in registers (lane i
+//     holds leaf row i; column values are broadcast with readlane);
+//     the panel below the leaf is solved against the leaf inverse and the
+//     trailing part of the block is updated, as 32 x 32 fp32-MFMA tiles;
+//   then L11^-1 is assembled from the leaf inverses: X_ba = -X_bb L_ba X_aa,
+//   first for 32-pairs, then for the two 64-halves.
+// The block is padded with an identity to 128 when m < 128.  X (lower) and
+// zeros (upper) are written back over the block.  A pivot that is not > 0
+// and finite sets *flag.
+constexpr int kDP = 130;            // LDS pitch (floats): conflict-light MFMA reads
+constexpr int kDiagThreads = 256;   // 4 wavefronts
+
+__device__ __forceinline__ float rl(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// acc += A(32 x K) * B(K x 32) with A(m,k) = a(m,k), B(k,n) = b(k,n), K even.
+template <typename FA, typename FB>
+__device__ __forceinline__ void mma32(f32x16_t &acc, int k0, int k1, int lane, FA a, FB b) {
+  for (int kk = k0; kk < k1; kk += 2) {
+    const int k = kk + (lane >> 5);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a(lane & 31, k), b(k, lane & 31), acc, 0, 0, 0);
+  }
+}
+
+// 32x32 MFMA result layout: element v of lane l is (row, col) =
+// (8*(v/4) + 4*(l/32) + v%4, l%32).
+template <typename F>
+__device__ __forceinline__ void for_acc(const f32x16_t &acc, int lane, F f) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) f(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), lane & 31, acc[v]);
+}
+
+__global__ void __launch_bounds__(kDiagThreads)
     potrf_inv_block_kernel(float *__restrict__ A, int64_t d, int64_t k0, int m,
                            int *__restrict__ flag) {
   extern __shared__ float sm[];
-  float *L = sm;               // kNB x kLP
-  float *X = sm + kNB * kLP;   // kNB x kLP
-  const int tid = threadIdx.x;
+  float *L = sm;              // 128 x kDP: the block, factored in place (lower)
+  float *X = sm + 128 * kDP;  // 128 x kDP: the inverse (lower)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float *Ab = A + k0 * d + k0;
-  for (int e = tid; e < m * m; e += kPotrfThreads) {
-    const int i = e / m, j = e % m;
-    L[i * kLP + j] = j <= i ? Ab[int64_t(i) * d + j] : 0.f;
-    X[i * kLP + j] = i == j ? 1.f : 0.f;
+  for (int e = tid; e < 128 * 128; e += kDiagThreads) {
+    const int i = e >> 7, j = e & 127;
+    float v;
+    if (i < m && j < m) v = j <= i ? Ab[int64_t(i) * d + j] : 0.f;
+    else v = i == j ? 1.f : 0.f;
+    L[i * kDP + j] = v;
+    X[i * kDP + j] = 0.f;
   }
   __syncthreads();
+
   bool bad = false;
-  for (int j = 0; j < m; ++j) {
-    const float piv = L[j * kLP + j];
-    const bool ok = piv > 0.f && piv <= 3.402823466e38f;
-    bad = bad || !ok;
-    const float ljj = ok ? sqrtf(piv) : 1.f;
-    __syncthreads();  // every thread has read the pivot
-    // column j of L, and row j of X scaled by 1/l_jj (X row j has entries in cols <= j)
-    for (int i = j + 1 + tid; i < m; i += kPotrfThreads) L[i * kLP + j] /= ljj;
-    for (int c = tid; c <= j; c += kPotrfThreads) X[j * kLP + c] /= ljj;
-    if (tid == 0) L[j * kLP + j] = ljj;
-    __syncthreads();
-    // trailing update of L (lower part of rows/cols > j) and elimination of
-    // X rows below j: X[i][c] -= L[i][j] * X[j][c] for c <= j.
-    const int rem = m - j - 1;
-    const int wide = j + 1;
-    for (int e = tid; e < rem * (rem + wide); e += kPotrfThreads) {
-      const int ii = e / (rem + wide), cc = e % (rem + wide);
-      const int i = j + 1 + ii;
-      const float lij = L[i * kLP + j];
-      if (cc < rem) {
-        const int k = j + 1 + cc;
-        if (k <= i) L[i * kLP + k] -= lij * L[k * kLP + j];
-      } else {
-        const int c = cc - rem;
-        X[i * kLP + c] -= lij * X[j * kLP + c];
+  for (int s = 0; s < 4; ++s) {
+    const int o = 32 * s;
+    if (wave == 0) {
+      const int i = lane & 31;
+      float a[32];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) a[k] = (lane < 32 && k <= i) ? L[(o + i) * kDP + o + k] : 0.f;
+      // leaf factor: column j scaled by 1/l_jj, then rank-1 update of the rest
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float piv = rl(a[j], j);
+        const bool ok = piv > 0.f && piv <= 3.402823466e38f;
+        bad = bad || !ok;
+        const float ljj = ok ? sqrtf(piv) : 1.f;
+        const float rinv = 1.f / ljj;
+        a[j] = (i == j) ? ljj : (i > j ? a[j] * rinv : a[j]);
+#pragma unroll
+        for (int k = j + 1; k < 32; ++k) {
+          const float lkj = rl(a[j], k);
+          if (i >= k) a[k] = fmaf(-a[j], lkj, a[k]);
+        }
+      }
+      // leaf inverse: lane c computes column c by forward substitution
+      float x[32];
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        float acc = (r == i) ? 1.f : 0.f;
+#pragma unroll
+        for (int k = 0; k < r; ++k) acc = fmaf(-rl(a[k], r), x[k], acc);
+        x[r] = acc / rl(a[r], r);
+      }
+      if (lane < 32) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) L[(o + i) * kDP + o + k] = k <= i ? a[k] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) X[(o + r) * kDP + o + i] = x[r];
       }
     }
     __syncthreads();
+    const int nb = 3 - s;  // 32-row blocks below the leaf
+    // panel: P_b = L[rows of b, leaf cols] * Xleaf^T
+    if (wave < nb) {
+      const int r0 = o + 32 + 32 * wave;
+      f32x16_t acc = {};
+      mma32(acc, 0, 32, lane, [&](int mm, int k) { return L[(r0 + mm) * kDP + o + k]; },
+            [&](int k, int n) { return X[(o + n) * kDP + o + k]; });
+      for_acc(acc, lane, [&](int r, int c, float v) { L[(r0 + r) * kDP + o + c] = v; });
+    }
+    __syncthreads();
+    // trailing part of the block: L[bi][bj] -= P_bi P_bj^T, bj <= bi
+    const int nblk = nb * (nb + 1) / 2;
+    for (int t = wave; t < nblk; t += 4) {
+      int bi = 0;
+      while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
+      const int bj = t - bi * (bi + 1) / 2;
+      const int ri = o + 32 + 32 * bi, rj = o + 32 + 32 * bj;
+      f32x16_t acc = {};
+      mma32(acc, 0, 32, lane, [&](int mm, int k) { return L[(ri + mm) * kDP + o + k]; },
+            [&](int k, int n) { return L[(rj + n) * kDP + o + k]; });
+      for_acc(acc, lane, [&](int r, int c, float v) {
+        if (bi != bj || r >= c) L[(ri + r) * kDP + rj + c] -= v;
+      });
+    }
+    __syncthreads();
   }
-  if (bad && tid == 0) *flag = 1;
-  for (int e = tid; e < m * m; e += kPotrfThreads) {
+
+  // ---- assemble L^-1 from the leaf inverses; scratch T lives in L's unused
+  //      upper triangle.
+  // level 1: pairs (0,1) and (2,3): X_ba = -X_bb (L_ba X_aa)
+  if (wave < 2) {
+    const int a0 = 64 * wave, b0 = a0 + 32;
+    float *T = L + a0 * kDP + b0;  // rows a0.., cols b0.. (above the diagonal)
+    f32x16_t acc = {};
+    mma32(acc, 0, 32, lane, [&](int mm, int k) { return L[(b0 + mm) * kDP + a0 + k]; },
+          [&](int k, int n) { return X[(a0 + k) * kDP + a0 + n]; });
+    for_acc(acc, lane, [&](int r, int c, float v) { T[r * kDP + c] = v; });
+    f32x16_t acc2 = {};
+    mma32(acc2, 0, 32, lane, [&](int mm, int k) { return X[(b0 + mm) * kDP + b0 + k]; },
+          [&](int k, int n) { return T[k * kDP + n]; });
+    for_acc(acc2, lane, [&](int r, int c, float v) { X[(b0 + r) * kDP + a0 + c] = -v; });
+  }
+  __syncthreads();
+  // level 2: halves [0,64) and [64,128): T = L[64:,:64] X[:64,:64]; X[64:,:64] = -X[64:,64:] T
+  {
+    float *T = L + 0 * kDP + 64;  // rows 0..63, cols 64..127 (above the diagonal)
+    const int bi = wave >> 1, bj = wave & 1;
+    f32x16_t acc = {};
+    // X[:64,:64] is lower in 32-blocks: block (kb, bj) is zero for kb < bj
+    mma32(acc, 32 * bj, 64, lane, [&](int mm, int k) { return L[(64 + 32 * bi + mm) * kDP + k]; },
+          [&](int k, int n) { return X[k * kDP + 32 * bj + n]; });
+    __syncthreads();
+    for_acc(acc, lane, [&](int r, int c, float v) { T[(32 * bi + r) * kDP + 32 * bj + c] = v; });
+    __syncthreads();
+    f32x16_t acc2 = {};
+    // X[64:,64:] is lower in 32-blocks: block (bi, kb) is zero for kb > bi
+    mma32(acc2, 0, 32 * (bi + 1), lane,
+          [&](int mm, int k) { return X[(64 + 32 * bi + mm) * kDP + 64 + k]; },
+          [&](int k, int n) { return T[k * kDP + 32 * bj + n]; });
+    for_acc(acc2, lane, [&](int r, int c, float v) { X[(64 + 32 * bi + r) * kDP + 32 * bj + c] = -v; });
+  }
+  __syncthreads();
+  if (tid == 0 && bad) *flag = 1;
+  for (int e = tid; e < m * m; e += kDiagThreads) {
     const int i = e / m, j = e % m;
-    Ab[int64_t(i) * d + j] = j <= i ? X[i * kLP + j] : 0.f;
+    Ab[int64_t(i) * d + j] = j <= i ? X[i * kDP + j] : 0.f;
   }
 }
 
@@ -244,7 +353,7 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
                   d, (const int32_t *)perm, (const uint8_t *)dead, (const double *)delta, A));
 
   // ---- blocked Cholesky A = L L^T; diagonal blocks end up holding L_ii^-1
-  const size_t lds = size_t(2) * kNB * kLP * sizeof(float);
+  const size_t lds = size_t(2) * 128 * kDP * sizeof(float);
   if (!g_lds_set) {
     hipError_t e = hipFuncSetAttribute((const void *)potrf_inv_block_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -254,7 +363,7 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
   }
   for (int64_t k0 = 0; k0 < d; k0 += kNB) {
     const int m = (int)std::min<int64_t>(kNB, d - k0);
-    GPTQ_TRY(launch("chol_diag_block", potrf_inv_block_kernel, dim3(1), dim3(kPotrfThreads), lds,
+    GPTQ_TRY(launch("chol_diag_block", potrf_inv_block_kernel, dim3(1), dim3(kDiagThreads), lds,
                     stream, A, d, k0, m, flag));
     const int64_t r = d - k0 - m;
     if (r <= 0) break;

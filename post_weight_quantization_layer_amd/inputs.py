@@ -9,8 +9,10 @@ Every element is a pure function of (seed, stream, row, token chunk):
 
 * W row ``i``           -> Philox key (seed, STREAM_W, i, 0)
 * X row ``i``, chunk c  -> Philox key (seed, STREAM_X, i, c), chunks of
-  ``TOKEN_CHUNK`` tokens; a chunk can be regenerated row by row, so a test can
-  rebuild any single feature row of a 131072-token X without the rest.
+  ``TOKEN_CHUNK`` tokens (the SiLU gate draws its second factor from
+  STREAM_X_GATE); a chunk can be regenerated row by row, and a token prefix
+  of a chunk needs only that many draws, so a test can rebuild any single
+  feature row of a 131072-token X without the rest.
 * outlier channels      -> Philox key (seed, STREAM_OUTLIER, 0, 0)
 
 Values are drawn as float32 standard normals; bf16 storage is obtained by
@@ -31,7 +33,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 TOKEN_CHUNK = 8192
-STREAM_W, STREAM_X, STREAM_OUTLIER = 0, 1, 2
+STREAM_W, STREAM_X, STREAM_OUTLIER, STREAM_X_GATE = 0, 1, 2, 3
 BASE_SEED = 20261203
 
 
@@ -166,14 +168,16 @@ def _row_scales(cfg: LayerConfig) -> np.ndarray:
     return s
 
 
-def _x_row_chunk(cfg: LayerConfig, row: int, chunk: int, scale: np.float32) -> np.ndarray:
-    """Full TOKEN_CHUNK tokens of feature ``row`` in chunk ``chunk`` (float32, pre-rounding)."""
+def _x_row_chunk(cfg: LayerConfig, row: int, chunk: int, scale: np.float32,
+                 upto: int = TOKEN_CHUNK) -> np.ndarray:
+    """The first ``upto`` tokens of feature ``row`` in chunk ``chunk`` (float32,
+    pre-rounding); a prefix of the chunk's values, whatever ``upto`` is."""
     g = _rng(cfg.seed, STREAM_X, row, chunk)
     if cfg.x_kind == "gauss":
-        v = g.standard_normal(TOKEN_CHUNK, dtype=np.float32)
+        v = g.standard_normal(upto, dtype=np.float32)
     elif cfg.x_kind == "silu_gated":
-        a = g.standard_normal(TOKEN_CHUNK, dtype=np.float32)
-        b = g.standard_normal(TOKEN_CHUNK, dtype=np.float32)
+        a = g.standard_normal(upto, dtype=np.float32)
+        b = _rng(cfg.seed, STREAM_X_GATE, row, chunk).standard_normal(upto, dtype=np.float32)
         with np.errstate(over="ignore"):
             v = (a / (np.float32(1) + np.exp(-a))) * b
     else:
@@ -197,7 +201,7 @@ def x_rows(cfg: LayerConfig, rows, tok0: int = 0, ntok: int | None = None) -> np
         for c in range(c0, c1):
             lo = max(tok0, c * TOKEN_CHUNK)
             hi = min(tok0 + ntok, (c + 1) * TOKEN_CHUNK)
-            v = _x_row_chunk(cfg, r, c, scales[r])[lo - c * TOKEN_CHUNK: hi - c * TOKEN_CHUNK]
+            v = _x_row_chunk(cfg, r, c, scales[r], hi - c * TOKEN_CHUNK)[lo - c * TOKEN_CHUNK:]
             out[k, lo - tok0: hi - tok0] = round_bf16(v) if cfg.x_dtype == "bf16" else v
 
     if len(rows) * (c1 - c0) > 64:

@@ -74,6 +74,17 @@ def classify_codes(q_gpu_p: np.ndarray, orc: "O.SweepResult", grid: str, group: 
                       unclassified=unclassified, max_step=step)
 
 
+def cascade_mask(q_gpu_p: np.ndarray, orc: "O.SweepResult", span: int) -> np.ndarray:
+    """Groups (rows x d/span) at or after the first differing code of their
+    row: there both sides follow different, equally valid, tie decisions, so
+    their grids are compared only for validity, not for equality."""
+    diff = q_gpu_p.astype(np.int64) != orc.q.astype(np.int64)
+    r, d = diff.shape
+    first = np.where(diff.any(axis=1), np.argmax(diff, axis=1), d)
+    g = np.arange(d // span)[None, :]
+    return g >= (first // span)[:, None]
+
+
 def assert_codes(rep: CodeReport, max_frac: float = 1e-3):
     assert rep.frac <= max_frac, f"{rep.mismatches}/{rep.n} codes differ"
     assert not rep.unclassified, f"mismatches not at a tie: {rep.unclassified[:5]}"
