@@ -6,7 +6,10 @@
 // owned by one workgroup that runs the whole token loop, so H is updated by
 // one read-modify-write per tile and the result is deterministic (no split-K
 // atomics).  X is d x n row-major (tokens contiguous), so both MFMA operands
-// are K-contiguous rows of X and no transpose is needed anywhere.
+// are K-contiguous rows of X and no transpose is needed anywhere.  X panels
+// stream into a 4-deep LDS ring with direct global->LDS copies; on diagonal
+// tiles the wave whose sub-tile lies below the diagonal accumulates the
+// float64 activation energy of the tile's rows from the same LDS data.
 #include "common.h"
 
 namespace gptq {
@@ -15,53 +18,68 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int kTile = 256;       // H tile edge
 constexpr int kBK = 32;          // tokens per pipeline stage
-constexpr int kThreads = 512;    // 8 waves: 2 along rows x 4 along cols
+constexpr int kThreads = 512;    // 8 waves (2 per SIMD), each a 128 x 64 sub-tile
+constexpr int kStages = 4;       // LDS ring depth (3 stages in flight)
 constexpr int kRowBytes = kBK * 2;                 // 64 B of one X row per stage
 constexpr int kPanelBytes = kTile * kRowBytes;     // 16 KB per operand per stage
+constexpr int kStageBytes = 2 * kPanelBytes;
 constexpr int kGroupRows = 4;    // tile-order band height (panel reuse in L2)
 
+// Wait until at most N vector-memory operations of this wave are in flight
+// (the global->LDS copies count as vector-memory operations).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+
 // 16-byte chunk position inside a 64-byte LDS row, XOR-swizzled so that the
-// MFMA operand reads (32 rows, same chunk) spread over all LDS banks.
+// MFMA operand reads (32 rows, same chunk) spread over the LDS banks.
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-template <bool kCheckK>
-__device__ __forceinline__ void load_panel(const uint16_t *__restrict__ X, int64_t ld, int64_t d,
-                                           int64_t n, int64_t row0, int64_t k0, int tid,
-                                           u32x4_t (&r)[2]) {
+// Copy one 256-row x 32-token panel of X into LDS with global_load_lds
+// (16 bytes per lane; lane l of an instruction lands at base + 16 l), two
+// 1 KB blocks per wave.  Slot s of the panel is row s/4, swizzled position
+// s%4, so each lane fetches the global chunk that belongs at its slot (four
+// lanes cover one row's 64 contiguous bytes).  Rows past d are clamped to
+// row d-1 (they only feed outputs that are never stored).
+__device__ __forceinline__ void issue_panel(const uint16_t *__restrict__ X, int64_t ld, int64_t d,
+                                            int64_t row0, int64_t k0, uint8_t *lds, int wave,
+                                            int lane) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int c = tid + kThreads * i;
-    const int rr = c >> 2, kc = c & 3;
-    const int64_t gr = row0 + rr;
-    const int64_t gk = k0 + kc * 8;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (gr < d) {
-      const uint16_t *p = X + gr * ld + gk;
-      if (!kCheckK || gk + 8 <= n) {
-        v = *reinterpret_cast<const u32x4_t *>(p);
-      } else {
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (gk + e < n) ? p[e] : 0u;
-        v[0] = h[0] | (h[1] << 16);
-        v[1] = h[2] | (h[3] << 16);
-        v[2] = h[4] | (h[5] << 16);
-        v[3] = h[6] | (h[7] << 16);
-      }
-    }
-    r[i] = v;
+    const int blk = wave * 2 + i;
+    const int slot = blk * 64 + lane;
+    const int r = slot >> 2, c = (slot & 3) ^ swz(r);
+    const int64_t gr = min(row0 + r, d - 1);
+    __builtin_amdgcn_global_load_lds((const void *)(X + gr * ld + k0 + c * 8),
+                                     LDS_PTR(lds + blk * 1024), 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ void store_panel(uint8_t *lds, int tid, const u32x4_t (&r)[2]) {
+// Ragged last stage: register path with element masks (tokens >= n are 0).
+__device__ __forceinline__ void tail_panel(const uint16_t *__restrict__ X, int64_t ld, int64_t d,
+                                           int64_t n, int64_t row0, int64_t k0, uint8_t *lds,
+                                           int tid) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int c = tid + kThreads * i;
-    const int rr = c >> 2, kc = c & 3;
-    *reinterpret_cast<u32x4_t *>(lds + rr * kRowBytes + ((kc ^ swz(rr)) << 4)) = r[i];
+    const int slot = tid + kThreads * i;
+    const int r = slot >> 2, c = (slot & 3) ^ swz(r);
+    const int64_t gr = min(row0 + r, d - 1);
+    const int64_t gk = k0 + c * 8;
+    const uint16_t *p = X + gr * ld + gk;
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = (gk + e < n) ? p[e] : 0u;
+    u32x4_t v;
+    v[0] = h[0] | (h[1] << 16);
+    v[1] = h[2] | (h[3] << 16);
+    v[2] = h[4] | (h[5] << 16);
+    v[3] = h[6] | (h[7] << 16);
+    *reinterpret_cast<u32x4_t *>(lds + slot * 16) = v;
   }
 }
 
@@ -76,12 +94,10 @@ __device__ __forceinline__ void tile_coords(int t, int nt, int &ti, int &tj) {
   int b0 = 0;
   while (true) {
     const int h = min(kGroupRows, nt - b0);
-    // tiles in this band: for tj in [b0, nt): rows b0 .. min(b0+h-1, tj)
     const int tri = h * (h + 1) / 2;            // tj in [b0, b0+h)
     const int rect = h * (nt - b0 - h);          // tj in [b0+h, nt)
     if (t < tri + rect) {
       if (t < tri) {
-        // tj = b0 + c, rows b0..b0+c: c*(c+1)/2 <= t < (c+1)(c+2)/2
         int c = 0;
         while ((c + 1) * (c + 2) / 2 <= t) ++c;
         tj = b0 + c;
@@ -98,9 +114,14 @@ __device__ __forceinline__ void tile_coords(int t, int nt, int &ti, int &tj) {
   }
 }
 
+__device__ __forceinline__ double bf16_to_f64(uint32_t bits16) {
+  return (double)__uint_as_float(bits16 << 16);
+}
+
 __global__ void __launch_bounds__(kThreads)
-    syrk_bf16_kernel(float *__restrict__ H, const uint16_t *__restrict__ X, int64_t d, int64_t n,
-                     int64_t ld, int nt, int ntiles, int per_xcd) {
+    syrk_bf16_kernel(float *__restrict__ H, double *__restrict__ hdiag,
+                     const uint16_t *__restrict__ X, int64_t d, int64_t n, int64_t ld, int nt,
+                     int ntiles, int per_xcd) {
   // XCD-aware mapping: workgroups are dealt round-robin to the 8 XCDs, so
   // give each XCD a contiguous run of the tile order (shared panels stay in
   // that XCD's L2).
@@ -115,14 +136,14 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t I0 = int64_t(ti) * kTile, J0 = int64_t(tj) * kTile;
 
   extern __shared__ __align__(16) uint8_t smem[];
-  // stage s: A panel at smem + 2s*P, B panel at smem + (2s+1)*P
-
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;   // wave tile: rows wm*128.., cols wn*64..
-  // On a diagonal tile the two lowest-left wave tiles lie strictly below the
-  // diagonal and are skipped.
-  const bool idle = diag && (wm * 128 > wn * 64 + 63);
+  const int wm = wave >> 2, wn = wave & 3;  // sub-tile rows wm*128.., cols wn*64..
+  // On a diagonal tile the two lower-left sub-tiles lie below the diagonal;
+  // those two waves accumulate the float64 activation energy of the tile's
+  // rows (128 rows each) from the same LDS data instead.
+  const bool energy = diag && wm == 1 && wn < 2;
+  const int erow0 = wn * 128;
 
   f32x16_t acc[4][2];
 #pragma unroll
@@ -131,55 +152,99 @@ __global__ void __launch_bounds__(kThreads)
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  double en[2] = {0.0, 0.0};
 
-  const int64_t nfull = n / kBK;
-  const int64_t nsteps = (n + kBK - 1) / kBK;
-  u32x4_t ra[2], rb[2];
-
-  auto load = [&](int64_t ks) {
-    const int64_t k0 = ks * kBK;
-    if (ks < nfull) {
-      load_panel<false>(X, ld, d, n, I0, k0, tid, ra);
-      if (!diag) load_panel<false>(X, ld, d, n, J0, k0, tid, rb);
-    } else {
-      load_panel<true>(X, ld, d, n, I0, k0, tid, ra);
-      if (!diag) load_panel<true>(X, ld, d, n, J0, k0, tid, rb);
-    }
+  auto issue = [&](int64_t ks) {
+    uint8_t *base = smem + (ks % kStages) * kStageBytes;
+    issue_panel(X, ld, d, I0, ks * kBK, base, wave, lane);
+    if (!diag) issue_panel(X, ld, d, J0, ks * kBK, base + kPanelBytes, wave, lane);
   };
-  auto store = [&](int s) {
-    store_panel(smem + (2 * s) * kPanelBytes, tid, ra);
-    if (!diag) store_panel(smem + (2 * s + 1) * kPanelBytes, tid, rb);
-  };
-
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int64_t ks = 0; ks < nsteps; ++ks) {
-    const int s = int(ks & 1);
-    if (ks + 1 < nsteps) load(ks + 1);
-    if (!idle) {
-      const uint8_t *A = smem + (2 * s) * kPanelBytes;
-      const uint8_t *B = diag ? A : A + kPanelBytes;
+  auto energy_stage = [&](const uint8_t *A) {
 #pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        const int chunk = kk * 2 + (lane >> 5);
-        bf16x8_t a[4], b[2];
+    for (int q = 0; q < 2; ++q) {
+      const int r = erow0 + lane + 64 * q;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = read_frag(A, wm * 128 + i * 32 + (lane & 31), chunk);
+      for (int c = 0; c < 4; ++c) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(A + r * kRowBytes + c * 16);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) b[j] = read_frag(B, wn * 64 + j * 32 + (lane & 31), chunk);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+          const double lo = bf16_to_f64(v[e] & 0xffffu), hi = bf16_to_f64(v[e] >> 16);
+          en[q] = fma(lo, lo, en[q]);
+          en[q] = fma(hi, hi, en[q]);
+        }
       }
     }
-    if (ks + 1 < nsteps) store(s ^ 1);
-    __syncthreads();
-  }
-  if (idle) return;
+  };
+  // One stage: fragments of both 16-token halves are read up front (the
+  // second half's reads overlap the first half's MFMAs); the stage's DMA for
+  // a later stage is issued between the reads and the MFMAs.
+  auto stage = [&](int buf, bool do_issue, int64_t next) {
+    const uint8_t *A = smem + buf * kStageBytes;
+    if (energy) {
+      if (do_issue) issue(next);
+      energy_stage(A);
+      return;
+    }
+    const uint8_t *B = diag ? A : A + kPanelBytes;
+    bf16x8_t a0[4], b0[2], a1[4], b1[2];
+    const int c0 = (lane >> 5), c1 = 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a0[i] = read_frag(A, wm * 128 + i * 32 + (lane & 31), c0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b0[j] = read_frag(B, wn * 64 + j * 32 + (lane & 31), c0);
+    if (do_issue) issue(next);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a1[i] = read_frag(A, wm * 128 + i * 32 + (lane & 31), c1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b1[j] = read_frag(B, wn * 64 + j * 32 + (lane & 31), c1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+  };
 
+  const int64_t nfull = n / kBK;
+  for (int64_t s = 0; s < nfull && s < kStages - 1; ++s) issue(s);
+  // per wave and stage: 2 copies per panel (1 panel on a diagonal tile)
+  for (int64_t ks = 0; ks < nfull; ++ks) {
+    // stage ks must have landed; stages ks+1, ks+2 may stay in flight
+    const int64_t ahead = min<int64_t>(2, nfull - 1 - ks);
+    if (diag) {
+      if (ahead == 2) vm_wait<4>();
+      else if (ahead == 1) vm_wait<2>();
+      else vm_wait<0>();
+    } else {
+      if (ahead == 2) vm_wait<8>();
+      else if (ahead == 1) vm_wait<4>();
+      else vm_wait<0>();
+    }
+    __builtin_amdgcn_s_barrier();  // all waves: stage ks landed, stage ks-1 consumed
+    stage(int(ks % kStages), ks + kStages - 1 < nfull, ks + kStages - 1);
+  }
+  if (nfull * kBK < n) {  // ragged token tail
+    vm_wait<0>();
+    __syncthreads();
+    uint8_t *base = smem + (nfull % kStages) * kStageBytes;
+    tail_panel(X, ld, d, n, I0, nfull * kBK, base, tid);
+    if (!diag) tail_panel(X, ld, d, n, J0, nfull * kBK, base + kPanelBytes, tid);
+    __syncthreads();
+    stage(int(nfull % kStages), false, 0);
+  }
+
+  if (energy) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int64_t r = I0 + erow0 + lane + 64 * q;
+      if (r < d) hdiag[r] += 2.0 * en[q];
+    }
+    return;
+  }
   // Epilogue: H[i][j] += 2 * acc for i <= j inside the matrix.  32x32 MFMA
   // result layout: lane l, element v -> row 8*(v/4) + 4*(l/32) + v%4, col l%32.
 #pragma unroll
@@ -278,11 +343,17 @@ gptq_status hessian_accumulate_impl(float *H, double *hdiag, int64_t d, const vo
     const int nt = (int)cdiv(d, kTile);
     const int ntiles = nt * (nt + 1) / 2;
     const int per_xcd = (int)cdiv(ntiles, 8);
-    const size_t lds = 4 * kPanelBytes;
-    GPTQ_TRY(launch("hessian_syrk_bf16", syrk_bf16_kernel, dim3(8 * per_xcd), dim3(kThreads),
-                    lds, stream, H, Xb, d, n_tok, ld_x, nt, ntiles, per_xcd));
-    GPTQ_TRY(launch("hessian_diag", diag_energy_kernel<uint16_t>, dim3((unsigned)d), dim3(256), 0,
-                    stream, hdiag, Xb, n_tok, ld_x));
+    const size_t lds = size_t(kStages) * kStageBytes;
+    static bool lds_set = false;
+    if (!lds_set) {
+      hipError_t e = hipFuncSetAttribute((const void *)syrk_bf16_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess)
+        return fail(GPTQ_ERR_DEVICE, std::string("cannot raise LDS limit: ") + hipGetErrorString(e));
+      lds_set = true;
+    }
+    GPTQ_TRY(launch("hessian_syrk_bf16", syrk_bf16_kernel, dim3(8 * per_xcd), dim3(kThreads), lds,
+                    stream, H, hdiag, Xb, d, n_tok, ld_x, nt, ntiles, per_xcd));
   } else {
     const float *Xf = static_cast<const float *>(X);
     const unsigned nt = (unsigned)cdiv(d, kFT);

@@ -193,13 +193,25 @@ __global__ void __launch_bounds__(kDiagThreads)
   float *X = sm + 128 * kDP;  // 128 x kDP: the inverse (lower)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float *Ab = A + k0 * d + k0;
-  for (int e = tid; e < 128 * 128; e += kDiagThreads) {
-    const int i = e >> 7, j = e & 127;
-    float v;
-    if (i < m && j < m) v = j <= i ? Ab[int64_t(i) * d + j] : 0.f;
-    else v = i == j ? 1.f : 0.f;
-    L[i * kDP + j] = v;
-    X[i * kDP + j] = 0.f;
+  // 64 elements per thread, loads issued 16 at a time so their latencies overlap
+  for (int t0 = 0; t0 < 64; t0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int e = tid + kDiagThreads * (t0 + t);
+      const int i = e >> 7, j = e & 127;
+      // unconditional load from a clamped (valid) address, select afterwards:
+      // no branch, so the 16 loads stay in flight together
+      const float g = Ab[int64_t(min(i, m - 1)) * d + min(j, m - 1)];
+      v[t] = (i < m && j <= i) ? g : (i == j && i >= m ? 1.f : 0.f);
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int e = tid + kDiagThreads * (t0 + t);
+      const int i = e >> 7, j = e & 127;
+      L[i * kDP + j] = v[t];
+      X[i * kDP + j] = 0.f;
+    }
   }
   __syncthreads();
 
@@ -211,29 +223,31 @@ __global__ void __launch_bounds__(kDiagThreads)
       float a[32];
 #pragma unroll
       for (int k = 0; k < 32; ++k) a[k] = (lane < 32 && k <= i) ? L[(o + i) * kDP + o + k] : 0.f;
-      // leaf factor: column j scaled by 1/l_jj, then rank-1 update of the rest
+      // leaf factor: column j scaled by 1/l_jj, then rank-1 update of the
+      // rest.  Entries above the diagonal (k > i) take part unmasked: they
+      // stay finite, are never read by the lower part, and are written as 0.
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
         const float piv = rl(a[j], j);
         const bool ok = piv > 0.f && piv <= 3.402823466e38f;
         bad = bad || !ok;
-        const float ljj = ok ? sqrtf(piv) : 1.f;
-        const float rinv = 1.f / ljj;
-        a[j] = (i == j) ? ljj : (i > j ? a[j] * rinv : a[j]);
+        const float ljj = ok ? __builtin_amdgcn_sqrtf(piv) : 1.f;
+        a[j] = (i == j) ? ljj : a[j] * __builtin_amdgcn_rcpf(ljj);
 #pragma unroll
-        for (int k = j + 1; k < 32; ++k) {
-          const float lkj = rl(a[j], k);
-          if (i >= k) a[k] = fmaf(-a[j], lkj, a[k]);
-        }
+        for (int k = j + 1; k < 32; ++k) a[k] = fmaf(-a[j], rl(a[j], k), a[k]);
       }
       // leaf inverse: lane c computes column c by forward substitution
       float x[32];
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
-        float acc = (r == i) ? 1.f : 0.f;
+        float acc0 = (r == i) ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
-        for (int k = 0; k < r; ++k) acc = fmaf(-rl(a[k], r), x[k], acc);
-        x[r] = acc / rl(a[r], r);
+        for (int k = 0; k + 1 < r; k += 2) {
+          acc0 = fmaf(-rl(a[k], r), x[k], acc0);
+          acc1 = fmaf(-rl(a[k + 1], r), x[k + 1], acc1);
+        }
+        if (r & 1) acc0 = fmaf(-rl(a[r - 1], r), x[r - 1], acc0);
+        x[r] = (acc0 + acc1) * __builtin_amdgcn_rcpf(rl(a[r], r));
       }
       if (lane < 32) {
 #pragma unroll
@@ -306,9 +320,11 @@ __global__ void __launch_bounds__(kDiagThreads)
   }
   __syncthreads();
   if (tid == 0 && bad) *flag = 1;
-  for (int e = tid; e < m * m; e += kDiagThreads) {
-    const int i = e / m, j = e % m;
-    Ab[int64_t(i) * d + j] = j <= i ? X[i * kDP + j] : 0.f;
+#pragma unroll 16
+  for (int t = 0; t < 64; ++t) {
+    const int e = tid + kDiagThreads * t;
+    const int i = e >> 7, j = e & 127;
+    if (i < m && j < m) Ab[int64_t(i) * d + j] = j <= i ? X[i * kDP + j] : 0.f;
   }
 }
 
