@@ -21,20 +21,23 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kT = 128;         // tile edge
-constexpr int kBK = 16;         // k per stage
+constexpr int kBK = 32;         // k per stage
 constexpr int kPitch = 132;     // LDS row pitch (floats) of a k-major stage
 constexpr int kThreads = 256;
 
+constexpr int kChunks = kT * kBK / 4 / kThreads;  // float4 chunks per thread per operand
+
 // Stage one operand tile (kT rows x kBK k, row-major in memory with leading
-// dimension ld) into registers: 512 float4 chunks, 2 per thread.  Elements
-// outside [0, rows) x [k0, kend) are zero.
+// dimension ld) into registers, kChunks float4 per thread.  Elements outside
+// [0, rows) x [k0, kend) are zero.
 template <bool kVec>
 __device__ __forceinline__ void load_rows(const float *__restrict__ P, int64_t ld, int rows,
-                                          int r0, int k0, int kend, int tid, f32x4_t (&v)[2]) {
+                                          int r0, int k0, int kend, int tid,
+                                          f32x4_t (&v)[kChunks]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kChunks; ++i) {
     const int c = tid + kThreads * i;
-    const int r = c >> 2, kc = (c & 3) * 4;
+    const int r = c / (kBK / 4), kc = (c % (kBK / 4)) * 4;
     const int gr = r0 + r, gk = k0 + kc;
     f32x4_t x = {0.f, 0.f, 0.f, 0.f};
     if (gr < rows) {
@@ -51,11 +54,11 @@ __device__ __forceinline__ void load_rows(const float *__restrict__ P, int64_t l
 }
 
 // Transposing store of a row-major staged tile into k-major LDS.
-__device__ __forceinline__ void store_rows_kmajor(float *lds, int tid, const f32x4_t (&v)[2]) {
+__device__ __forceinline__ void store_rows_kmajor(float *lds, int tid, const f32x4_t (&v)[kChunks]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kChunks; ++i) {
     const int c = tid + kThreads * i;
-    const int r = c >> 2, kc = (c & 3) * 4;
+    const int r = c / (kBK / 4), kc = (c % (kBK / 4)) * 4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) lds[(kc + e) * kPitch + r] = v[i][e];
   }
@@ -64,9 +67,10 @@ __device__ __forceinline__ void store_rows_kmajor(float *lds, int tid, const f32
 // B in row-major K x N: a tile (kBK k-rows x kT cols) is already k-major.
 template <bool kVec>
 __device__ __forceinline__ void load_kmajor(const float *__restrict__ P, int64_t ld, int cols,
-                                            int c0, int k0, int kend, int tid, f32x4_t (&v)[2]) {
+                                            int c0, int k0, int kend, int tid,
+                                            f32x4_t (&v)[kChunks]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kChunks; ++i) {
     const int c = tid + kThreads * i;
     const int k = c >> 5, nc = (c & 31) * 4;
     const int gk = k0 + k, gc = c0 + nc;
@@ -84,9 +88,9 @@ __device__ __forceinline__ void load_kmajor(const float *__restrict__ P, int64_t
   }
 }
 
-__device__ __forceinline__ void store_kmajor(float *lds, int tid, const f32x4_t (&v)[2]) {
+__device__ __forceinline__ void store_kmajor(float *lds, int tid, const f32x4_t (&v)[kChunks]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kChunks; ++i) {
     const int c = tid + kThreads * i;
     const int k = c >> 5, nc = (c & 31) * 4;
     *reinterpret_cast<f32x4_t *>(lds + k * kPitch + nc) = v[i];
@@ -133,8 +137,26 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmGroup g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // C tile prefetch (beta != 0): unconditional loads from clamped, valid
+  // addresses, issued before the K loop so their latency overlaps it.
+  const float alpha = P.alpha, beta = P.beta;
+  float cv[2][2][16];
+  if (beta != 0.f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int gc = min(n0 + wn * 64 + j * 32 + (lane & 31), P.N - 1);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int gr = min(m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), P.M - 1);
+          cv[i][j][v] = P.C[int64_t(gr) * P.ldc + gc];
+        }
+      }
+  }
+
   const int nsteps = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
-  f32x4_t ra[2], rb[2];
+  f32x4_t ra[kChunks], rb[kChunks];
   auto load = [&](int s) {
     const int k0 = kbeg + s * kBK;
     load_rows<kVec>(P.A, P.lda, P.M, m0, k0, kend, tid, ra);
@@ -179,23 +201,20 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmGroup g) {
     }
   }
 
-  // ---- epilogue.  32x32 result layout: lane l, element v ->
+  // ---- epilogue (stores only).  32x32 result layout: lane l, element v ->
   //      row 8*(v/4) + 4*(l/32) + v%4, col l%32.
-  const float alpha = P.alpha, beta = P.beta;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int gc = n0 + wn * 64 + j * 32 + (lane & 31);
-      if (gc >= P.N) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int gr = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (gr >= P.M) continue;
-        if (g.lower_out && gr < gc) continue;
-        float *c = P.C + int64_t(gr) * P.ldc + gc;
         const float r = alpha * acc[i][j][v];
-        *c = (beta == 0.f) ? r : r + beta * *c;
+        const float out = (beta == 0.f) ? r : fmaf(beta, cv[i][j][v], r);
+        if (gr < P.M && gc < P.N && (!g.lower_out || gr >= gc))
+          P.C[int64_t(gr) * P.ldc + gc] = out;
       }
     }
 }

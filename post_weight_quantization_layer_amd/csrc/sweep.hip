@@ -24,7 +24,7 @@ namespace gptq {
 namespace {
 
 constexpr int kMaxB = 128;
-constexpr int kSweepThreads = 512;  // 8 wavefronts, one row each at a time
+constexpr int kSweepThreads = 256;  // 4 wavefronts, 4 rows each at a time
 constexpr int kSweepMaxWG = 512;
 
 struct SweepArgs {
@@ -81,184 +81,337 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
   return __uint_as_float(sign | ((e + 112u) << 23) | (m << 13));
 }
 
-template <int kQ4K>
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// rint(num / den) exactly as if num / den were computed with a correctly
+// rounded IEEE division: the quotient is formed as num * rden (rden ~ 1/den)
+// and only when that lands within 1e-5 of a half-integer -- where the two
+// roundings could disagree -- is the IEEE division done.  |num/den| <= 32 is
+// all that matters here (larger values are clamped away); there the product
+// is within 3 ulp (< 6e-6) of the IEEE quotient.  The exact path is a
+// wavefront-uniform branch taken only when some lane is near a tie.
+__device__ __forceinline__ float rint_div(float num, float den, float rden) {
+  const float y = num * rden;
+  float r = __builtin_rintf(y);
+  const bool near = fabsf(y - floorf(y) - 0.5f) < 1e-5f;
+  if (__builtin_expect(__any(near), 0)) r = near ? __builtin_rintf(num / den) : r;
+  return r;
+}
+
+// Row groups: a wavefront sweeps 4 rows at once, 16 lanes per row, each
+// lane owning 8 contiguous block columns (B <= 128).  The per-column chain
+// (quantize w_j, error, update) is computed by the 16 lanes of a row group
+// together, so every instruction of the chain serves 4 rows.
+constexpr int kLPR = 16;  // lanes per row
+constexpr int kCPL = 8;   // columns per lane
+
+__device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src); }
+
+// Value of sub-lane `sub` of this lane's row group, for all four groups at
+// once: four readlanes (VALU, no LDS round trip) and a select.
+__device__ __forceinline__ float group_bcast(float v, int sub, int grp) {
+  const float g0 = bcast(v, sub), g1 = bcast(v, 16 + sub);
+  const float g2 = bcast(v, 32 + sub), g3 = bcast(v, 48 + sub);
+  return grp < 2 ? (grp == 0 ? g0 : g1) : (grp == 2 ? g2 : g3);
+}
+
+__device__ __forceinline__ float group_min(float v) {
+#pragma unroll
+  for (int off = 1; off < kLPR; off <<= 1) v = fminf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int off = 1; off < kLPR; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// kG8: the group size is a multiple of 8, so groups start only at the first
+// column of an 8-column step (the check runs once per 8 columns).
+template <int kQ4K, bool kG8>
 __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
-  extern __shared__ float Ub[];  // B x kMaxB, upper part of U's block
+  // LDS: U's block (rows 0 .. Bp-1 of kMaxB floats, Bp = B rounded up to 8,
+  // rows and columns past B zero), then Bp reciprocals of the diagonal
+  // (zero past B, so padding steps change nothing).
+  extern __shared__ float Ub[];
+  const int Bp = (a.B + 7) & ~7;
+  float *Uinv = Ub + (Bp + 1) * kMaxB;
   const int tid = threadIdx.x;
   const int B = a.B;
   const int64_t ld = a.cols;
-  for (int e = tid; e < B * B; e += kSweepThreads) {
-    const int j = e / B, k = e % B;
-    Ub[j * kMaxB + k] = k >= j ? a.U[int64_t(a.i1 + j) * ld + a.i1 + k] : 0.f;
+  // U block: rows i1 .. i1+B-1, columns i1 .. i1+B-1.  Loads are issued in
+  // batches (all before any use) so their latencies overlap.
+  const float *Ublk = a.U + int64_t(a.i1) * ld + a.i1;
+  if ((ld & 3) == 0 && (a.i1 & 3) == 0 && (B & 3) == 0) {
+    const int nq = B * B / 4;  // float4 chunks (B/4 per row)
+    for (int e0 = tid; e0 < nq; e0 += kSweepThreads * 8) {
+      f32x4_t v[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int e = min(e0 + t * kSweepThreads, nq - 1);
+        const int j = e / (B / 4), k = (e % (B / 4)) * 4;
+        v[t] = *reinterpret_cast<const f32x4_t *>(Ublk + int64_t(j) * ld + k);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int e = e0 + t * kSweepThreads;
+        if (e < nq) {
+          const int j = e / (B / 4), k = (e % (B / 4)) * 4;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            Ub[j * kMaxB + k + x] = (k + x >= j) ? v[t][x] : 0.f;
+            if (k + x == j) Uinv[j] = 1.f / v[t][x];
+          }
+        }
+      }
+    }
+  } else {
+    for (int e = tid; e < B * B; e += kSweepThreads) {
+      const int j = e / B, k = e % B;
+      const float u = Ublk[int64_t(j) * ld + k];
+      Ub[j * kMaxB + k] = k >= j ? u : 0.f;
+      if (k == j) Uinv[j] = 1.f / u;
+    }
   }
+  // columns past B of rows < B, and the padding rows B .. Bp (one extra row
+  // is read by the one-step-ahead prefetch), are zero
+  for (int e = tid; e < B * (kMaxB - B); e += kSweepThreads)
+    Ub[(e / (kMaxB - B)) * kMaxB + B + e % (kMaxB - B)] = 0.f;
+  for (int e = tid; e < (Bp + 1 - B) * kMaxB; e += kSweepThreads) Ub[B * kMaxB + e] = 0.f;
+  for (int j = B + tid; j < Bp + 1; j += kSweepThreads) Uinv[j] = 0.f;
   __syncthreads();
 
   const int lane = tid & 63, wave = tid >> 6;
-  const int64_t nwaves = int64_t(gridDim.x) * (kSweepThreads / 64);
+  const int grp = lane >> 4, sl = lane & 15;
+  const int gbase = lane & 48;  // first lane of this row group
+  const int c0 = sl * kCPL;     // first block column owned by this lane
   const int G = kQ4K ? 256 : a.group;
   const float maxq = float((1 << a.bits) - 1);
-  const bool v0 = lane < B, v1 = lane + 64 < B;
   const int64_t ngroups = a.cols / G;
+  const int64_t rows_per_pass = int64_t(gridDim.x) * (kSweepThreads / 64) * 4;
+  // 16-byte W accesses need a 4-float aligned row stride and block start
+  const bool vec = (ld & 3) == 0 && (a.i1 & 3) == 0;
 
-  for (int64_t row = int64_t(blockIdx.x) * (kSweepThreads / 64) + wave; row < a.rows;
-       row += nwaves) {
-    float *wrow = a.W + row * ld + a.i1;
-    float w0 = v0 ? wrow[lane] : 0.f;
-    float w1 = v1 ? wrow[64 + lane] : 0.f;
-    float q0 = 0.f, q1 = 0.f, e0 = 0.f, e1 = 0.f;
+  for (int64_t r0 = (int64_t(blockIdx.x) * (kSweepThreads / 64) + wave) * 4; r0 < a.rows;
+       r0 += rows_per_pass) {
+    const int64_t row = r0 + grp;
+    const bool rv = row < a.rows;  // whole row group is valid or not
+    const int64_t rowc = rv ? row : a.rows - 1;
+    float *wrow = a.W + rowc * ld + a.i1;
+    float w[kCPL], q[kCPL], e[kCPL];
+    if (vec && c0 + kCPL <= B) {
+      const f32x4_t t0 = *reinterpret_cast<const f32x4_t *>(wrow + c0);
+      const f32x4_t t1 = *reinterpret_cast<const f32x4_t *>(wrow + c0 + 4);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        w[x] = t0[x];
+        w[4 + x] = t1[x];
+      }
+    } else {
+#pragma unroll
+      for (int x = 0; x < kCPL; ++x) w[x] = (c0 + x < B) ? wrow[c0 + x] : 0.f;
+    }
+#pragma unroll
+    for (int x = 0; x < kCPL; ++x) q[x] = e[x] = 0.f;
 
-    // grid state of the current group
-    float s = 1.f, z = 0.f;           // affine
-    float Sv = 0.f, Mv = 0.f;         // q4k: lane b < 8 holds S_b, M_b
+    // grid state of the current group (per row group, identical in its lanes)
+    float s = 1.f, rs = 1.f, z = 0.f;       // affine
+    float Sv = 0.f, Mv = 0.f, rSv = 0.f;    // q4k: sub-lane b < 8 holds S_b, M_b, 1/S_b
 
     if (a.i1 % G != 0) {  // group began in an earlier block: read its grid back
       const int64_t gi = a.i1 / G;
       if (!kQ4K) {
-        s = a.scale[row * ngroups + gi];
-        z = float(a.zero[row * ngroups + gi]);
+        s = a.scale[rowc * ngroups + gi];
+        rs = 1.f / s;
+        z = float(a.zero[rowc * ngroups + gi]);
       } else {
-        const float Df = f16_to_f32(a.D[row * ngroups + gi]);
-        const float Dmf = f16_to_f32(a.Dm[row * ngroups + gi]);
-        if (lane < 8) {
-          const int64_t sb = row * (a.cols / 32) + gi * 8 + lane;
-          Sv = Df * float(a.sc[sb]);
-          Mv = Dmf * float(a.mc[sb]);
-        }
+        const float Df = f16_to_f32(a.D[rowc * ngroups + gi]);
+        const float Dmf = f16_to_f32(a.Dm[rowc * ngroups + gi]);
+        const int64_t sb = rowc * (a.cols / 32) + gi * 8 + (sl & 7);
+        Sv = Df * float(a.sc[sb]);
+        Mv = Dmf * float(a.mc[sb]);
+        rSv = Sv > 0.f ? 1.f / Sv : 0.f;
       }
     }
 
-    for (int j = 0; j < B; ++j) {
+    // next block column at which a group starts (scalar counter, no division)
+    int jg = (G - a.i1 % G) % G;
+    // choose the grid of the group starting at block column j (from the
+    // current, compensated weights)
+    auto choose_grid = [&](int j) {
       const int col = a.i1 + j;
-      if (col % G == 0) {
-        const int64_t gi = col / G;
+      const int64_t gi = col / G;
+          if (!kQ4K) {
+            float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+            for (int y = 0; y < kCPL; ++y) {
+              const int c = c0 + y;
+              if (c < B && c >= j && c < j + G) {
+                mn = fminf(mn, w[y]);
+                mx = fmaxf(mx, w[y]);
+              }
+            }
+            for (int c = B + sl; c < j + G; c += kLPR) {  // group reaches past the block
+              const float v = wrow[c];
+              mn = fminf(mn, v);
+              mx = fmaxf(mx, v);
+            }
+            mn = group_min(mn);
+            mx = group_max(mx);
+            float xmin = fminf(mn, 0.f), xmax = fmaxf(mx, 0.f);
+            if (xmin == xmax) {
+              xmin = -1.f;
+              xmax = 1.f;
+            }
+            s = (xmax - xmin) / maxq;
+            rs = 1.f / s;
+            z = fminf(fmaxf(__builtin_rintf(-xmin / s), 0.f), maxq);
+            if (sl == 0 && rv) {
+              a.scale[row * ngroups + gi] = s;
+              a.zero[row * ngroups + gi] = (uint8_t)z;
+            }
+          } else {
+            // super-block of 256 starting here (always a block start): the
+            // lane's columns 128t + c0 + y for t = 0, 1; sub-block
+            // b = 4t + sl/4 is a group of 4 lanes.
+            float sb_s[2], sb_m[2];
+            float smax = 0.f, mmax = 0.f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+              for (int y = 0; y < kCPL; ++y) {
+                const int p = 128 * t + c0 + y;
+                const float v = (p < B) ? w[y] : wrow[p];
+                mn = fminf(mn, v);
+                mx = fmaxf(mx, v);
+              }
+              mn = fminf(mn, __shfl_xor(mn, 1));
+              mn = fminf(mn, __shfl_xor(mn, 2));
+              mx = fmaxf(mx, __shfl_xor(mx, 1));
+              mx = fmaxf(mx, __shfl_xor(mx, 2));
+              mn = fminf(mn, 0.f);
+              mx = fmaxf(mx, 0.f);
+              sb_s[t] = (mx - mn) / 15.f;
+              sb_m[t] = -mn;
+              smax = fmaxf(smax, sb_s[t]);
+              mmax = fmaxf(mmax, sb_m[t]);
+            }
+            smax = group_max(smax);
+            mmax = group_max(mmax);
+            const uint16_t Dh = f32_to_f16_rne(smax / 63.f);
+            const uint16_t Dmh = f32_to_f16_rne(mmax / 63.f);
+            const float Df = f16_to_f32(Dh), Dmf = f16_to_f32(Dmh);
+            float Sb[2], Mb[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const float scq = (sb_s[t] > 0.f && Df > 0.f)
+                                    ? fminf(fmaxf(__builtin_rintf(sb_s[t] / Df), 1.f), 63.f)
+                                    : 0.f;
+              const float mcq =
+                  (Dmf > 0.f) ? fminf(fmaxf(__builtin_rintf(sb_m[t] / Dmf), 0.f), 63.f) : 0.f;
+              Sb[t] = Df * scq;
+              Mb[t] = Dmf * mcq;
+              if ((sl & 3) == 0 && rv) {
+                const int b = 4 * t + (sl >> 2);
+                const int64_t o = row * (a.cols / 32) + gi * 8 + b;
+                a.sc[o] = (uint8_t)scq;
+                a.mc[o] = (uint8_t)mcq;
+              }
+            }
+            if (sl == 0 && rv) {
+              a.D[row * ngroups + gi] = Dh;
+              a.Dm[row * ngroups + gi] = Dmh;
+            }
+            // sub-lane b < 8 <- S_b, M_b: b = 4t + g is held by sub-lane 4g of half t
+            const int src = gbase + 4 * (sl & 3);
+            const float S0 = shfl(Sb[0], src), S1 = shfl(Sb[1], src);
+            const float M0 = shfl(Mb[0], src), M1 = shfl(Mb[1], src);
+            Sv = (sl & 4) ? S1 : S0;
+            Mv = (sl & 4) ? M1 : M0;
+            rSv = Sv > 0.f ? 1.f / Sv : 0.f;
+          }
+    };
+    // U row j and 1/U_jj, fetched one step ahead
+    f32x4_t un0 = *reinterpret_cast<const f32x4_t *>(Ub + c0);
+    f32x4_t un1 = *reinterpret_cast<const f32x4_t *>(Ub + c0 + 4);
+    float uin = Uinv[0];
+    for (int j8 = 0; j8 < Bp; j8 += kCPL) {
+      if (kG8 && j8 == jg && j8 < B) {
+        jg += G;
+        choose_grid(j8);
+      }
+      const bool own = sl == (j8 >> 3);  // this lane owns columns j8 .. j8+7
+#pragma unroll
+      for (int x = 0; x < kCPL; ++x) {
+        const int j = j8 + x;
+        const int col = a.i1 + j;
+        const f32x4_t u0 = un0, u1 = un1;
+        const float uinv = uin;
+        un0 = *reinterpret_cast<const f32x4_t *>(Ub + (j + 1) * kMaxB + c0);
+        un1 = *reinterpret_cast<const f32x4_t *>(Ub + (j + 1) * kMaxB + c0 + 4);
+        uin = Uinv[j + 1];
+        if (!kG8 && j == jg && j < B) {
+          jg += G;
+          choose_grid(j);
+        }
+        const float wj = group_bcast(w[x], j >> 3, grp);
+        float qj, wq;
         if (!kQ4K) {
-          float mn = INFINITY, mx = -INFINITY;
-          if (v0 && lane >= j && lane < j + G) {
-            mn = w0;
-            mx = w0;
-          }
-          if (v1 && lane + 64 >= j && lane + 64 < j + G) {
-            mn = fminf(mn, w1);
-            mx = fmaxf(mx, w1);
-          }
-          for (int c = B + lane; c < j + G; c += 64) {  // group reaches past the block
-            const float v = wrow[c];
-            mn = fminf(mn, v);
-            mx = fmaxf(mx, v);
-          }
-          mn = wave_min(mn, 64);
-          mx = wave_max(mx, 64);
-          float xmin = fminf(mn, 0.f), xmax = fmaxf(mx, 0.f);
-          if (xmin == xmax) {
-            xmin = -1.f;
-            xmax = 1.f;
-          }
-          s = (xmax - xmin) / maxq;
-          z = fminf(fmaxf(__builtin_rintf(-xmin / s), 0.f), maxq);
-          if (lane == 0) {
-            a.scale[row * ngroups + gi] = s;
-            a.zero[row * ngroups + gi] = (uint8_t)z;
-          }
+          qj = fminf(fmaxf(rint_div(wj, s, rs) + z, 0.f), maxq);
+          wq = s * (qj - z);
         } else {
-          // super-block of 256 starting at this column (always a block start)
-          float sb_s[4], sb_m[4];
-          float smax = 0.f, mmax = 0.f;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int p = lane + 64 * t;
-            float v;
-            if (p < B) v = (t == 0) ? w0 : w1;
-            else v = wrow[p];
-            float mn = wave_min(v, 32), mx = wave_max(v, 32);
-            mn = fminf(mn, 0.f);
-            mx = fmaxf(mx, 0.f);
-            sb_s[t] = (mx - mn) / 15.f;
-            sb_m[t] = -mn;
-            smax = fmaxf(smax, sb_s[t]);
-            mmax = fmaxf(mmax, sb_m[t]);
-          }
-          smax = fmaxf(smax, __shfl_xor(smax, 32));
-          mmax = fmaxf(mmax, __shfl_xor(mmax, 32));
-          const uint16_t Dh = f32_to_f16_rne(smax / 63.f);
-          const uint16_t Dmh = f32_to_f16_rne(mmax / 63.f);
-          const float Df = f16_to_f32(Dh), Dmf = f16_to_f32(Dmh);
-          float Sb[4], Mb[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float scq = (sb_s[t] > 0.f && Df > 0.f)
-                                  ? fminf(fmaxf(__builtin_rintf(sb_s[t] / Df), 1.f), 63.f)
-                                  : 0.f;
-            const float mcq =
-                (Dmf > 0.f) ? fminf(fmaxf(__builtin_rintf(sb_m[t] / Dmf), 0.f), 63.f) : 0.f;
-            Sb[t] = Df * scq;
-            Mb[t] = Dmf * mcq;
-            if ((lane & 31) == 0) {
-              const int b = 2 * t + (lane >> 5);
-              const int64_t o = row * (a.cols / 32) + gi * 8 + b;
-              a.sc[o] = (uint8_t)scq;
-              a.mc[o] = (uint8_t)mcq;
-            }
-          }
-          if (lane == 0) {
-            a.D[row * ngroups + gi] = Dh;
-            a.Dm[row * ngroups + gi] = Dmh;
-          }
-          // lane b < 8 <- S_b, M_b (b = 2t + half)
-          float sv = 0.f, mv = 0.f;
-#pragma unroll
-          for (int b = 0; b < 8; ++b) {
-            const float S_ = bcast(Sb[b >> 1], (b & 1) * 32);
-            const float M_ = bcast(Mb[b >> 1], (b & 1) * 32);
-            if (lane == b) {
-              sv = S_;
-              mv = M_;
-            }
-          }
-          Sv = sv;
-          Mv = mv;
+          const int bsub = (col & 255) >> 5;
+          const float S = group_bcast(Sv, bsub, grp), M = group_bcast(Mv, bsub, grp);
+          qj = (S > 0.f) ? fminf(fmaxf(rint_div(wj + M, S, group_bcast(rSv, bsub, grp)), 0.f), 15.f)
+                         : 0.f;
+          wq = S * qj - M;
         }
+        const float ej = (wj - wq) * uinv;
+        // No masks: U's block row j is zero left of the diagonal (and past B),
+        // and the owner's column j is overwritten with w^_j just below.
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          w[y] = fmaf(-ej, u0[y], w[y]);
+          w[4 + y] = fmaf(-ej, u1[y], w[4 + y]);
+        }
+        w[x] = own ? wq : w[x];
+        q[x] = own ? qj : q[x];
+        e[x] = own ? ej : e[x];
       }
+    }
 
-      const float wj = bcast(j < 64 ? w0 : w1, j & 63);
-      float qj, wq;
-      if (!kQ4K) {
-        qj = fminf(fmaxf(__builtin_rintf(wj / s) + z, 0.f), maxq);
-        wq = s * (qj - z);
+    if (rv) {
+      uint8_t *qrow = a.q + row * ld + a.i1;
+      float *erow = a.Err + row * kMaxB;
+      if (c0 + kCPL <= B) {
+        *reinterpret_cast<f32x4_t *>(erow + c0) = f32x4_t{e[0], e[1], e[2], e[3]};
+        *reinterpret_cast<f32x4_t *>(erow + c0 + 4) = f32x4_t{e[4], e[5], e[6], e[7]};
       } else {
-        const int b = (col & 255) >> 5;
-        const float S = bcast(Sv, b), M = bcast(Mv, b);
-        qj = (S > 0.f) ? fminf(fmaxf(__builtin_rintf((wj + M) / S), 0.f), 15.f) : 0.f;
-        wq = S * qj - M;
+#pragma unroll
+        for (int x = 0; x < kCPL; ++x)
+          if (c0 + x < B) erow[c0 + x] = e[x];
       }
-      const float ej = (wj - wq) / Ub[j * kMaxB + j];
-      const float u0 = Ub[j * kMaxB + lane];
-      const float u1 = Ub[j * kMaxB + 64 + lane];
-      if (v0 && lane > j) w0 = fmaf(-ej, u0, w0);
-      if (v1 && lane + 64 > j) w1 = fmaf(-ej, u1, w1);
-      if (lane == (j & 63)) {
-        if (j < 64) {
-          w0 = wq;
-          q0 = qj;
-          e0 = ej;
-        } else {
-          w1 = wq;
-          q1 = qj;
-          e1 = ej;
+      if (vec && c0 + kCPL <= B) {
+        *reinterpret_cast<f32x4_t *>(wrow + c0) = f32x4_t{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<f32x4_t *>(wrow + c0 + 4) = f32x4_t{w[4], w[5], w[6], w[7]};
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          lo |= uint32_t(q[x]) << (8 * x);
+          hi |= uint32_t(q[4 + x]) << (8 * x);
         }
+        *reinterpret_cast<uint32_t *>(qrow + c0) = lo;
+        *reinterpret_cast<uint32_t *>(qrow + c0 + 4) = hi;
+      } else {
+#pragma unroll
+        for (int x = 0; x < kCPL; ++x)
+          if (c0 + x < B) {
+            wrow[c0 + x] = w[x];
+            qrow[c0 + x] = (uint8_t)q[x];
+          }
       }
-    }
-
-    uint8_t *qrow = a.q + row * ld + a.i1;
-    float *erow = a.Err + row * kMaxB;
-    if (v0) {
-      wrow[lane] = w0;
-      qrow[lane] = (uint8_t)q0;
-      erow[lane] = e0;
-    }
-    if (v1) {
-      wrow[64 + lane] = w1;
-      qrow[64 + lane] = (uint8_t)q1;
-      erow[64 + lane] = e1;
     }
   }
 }
@@ -305,7 +458,7 @@ __global__ void __launch_bounds__(256)
   if (p < cols) g_idx[perm[p]] = (int32_t)(p / gsz);
 }
 
-bool g_sweep_lds_set[2] = {false, false};
+bool g_sweep_lds_set[4] = {false, false, false, false};
 
 }  // namespace
 
@@ -344,16 +497,20 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
 
   const int q4k = p.grid == GPTQ_GRID_Q4K;
   const int B = p.block;
-  const size_t lds = size_t(B) * kMaxB * sizeof(float);
-  if (lds > 65536 && !g_sweep_lds_set[q4k]) {
-    hipError_t e = hipFuncSetAttribute(
-        q4k ? (const void *)sweep_kernel<1> : (const void *)sweep_kernel<0>,
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const size_t Bp = (B + 7) & ~7;
+  const size_t lds = ((Bp + 1) * kMaxB + Bp + 1) * sizeof(float);
+  const int g8 = (q4k ? 256 : p.group) % 8 == 0;
+  const int variant = q4k * 2 + g8;
+  const void *kfn[4] = {(const void *)sweep_kernel<0, false>, (const void *)sweep_kernel<0, true>,
+                        (const void *)sweep_kernel<1, false>, (const void *)sweep_kernel<1, true>};
+  if (lds > 65536 && !g_sweep_lds_set[variant]) {
+    hipError_t e = hipFuncSetAttribute(kfn[variant], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
     if (e != hipSuccess)
       return fail(GPTQ_ERR_DEVICE, std::string("cannot raise LDS limit: ") + hipGetErrorString(e));
-    g_sweep_lds_set[q4k] = true;
+    g_sweep_lds_set[variant] = true;
   }
-  const unsigned nwg = (unsigned)std::min<int64_t>(cdiv(rows, kSweepThreads / 64), kSweepMaxWG);
+  const unsigned nwg = (unsigned)std::min<int64_t>(cdiv(rows, kSweepThreads / 64 * 4), kSweepMaxWG);
 
   SweepArgs a{};
   a.W = Wp;
@@ -374,11 +531,14 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
     const int Bc = (int)std::min<int64_t>(B, cols - i1);
     a.i1 = (int)i1;
     a.B = Bc;
-    if (q4k)
-      GPTQ_TRY(launch("sweep_q4k", sweep_kernel<1>, dim3(nwg), dim3(kSweepThreads), lds, stream, a));
-    else
-      GPTQ_TRY(launch("sweep_affine", sweep_kernel<0>, dim3(nwg), dim3(kSweepThreads), lds, stream,
-                      a));
+    const char *nm = q4k ? "sweep_q4k" : "sweep_affine";
+    const dim3 grid(nwg), blk(kSweepThreads);
+    switch (variant) {
+      case 0: GPTQ_TRY(launch(nm, sweep_kernel<0, false>, grid, blk, lds, stream, a)); break;
+      case 1: GPTQ_TRY(launch(nm, sweep_kernel<0, true>, grid, blk, lds, stream, a)); break;
+      case 2: GPTQ_TRY(launch(nm, sweep_kernel<1, false>, grid, blk, lds, stream, a)); break;
+      default: GPTQ_TRY(launch(nm, sweep_kernel<1, true>, grid, blk, lds, stream, a)); break;
+    }
     const int64_t i2 = i1 + Bc;
     if (i2 < cols) {
       GPTQ_TRY(gemm_f32(Err, kMaxB, U + i1 * cols + i2, cols, Wp + i2, cols, (int)rows,

@@ -104,3 +104,20 @@ def test_block_group_combinations(block, group):
     log(f"[edges] B={block} g={group}: {rep.mismatches} code mismatches")
     assert_codes(rep)
     assert rel_fro(g.U, o.U) <= 1e-4
+
+
+@pytest.mark.parametrize("act", [False, True])
+def test_odd_width_small_groups(act):
+    """An odd number of columns (scalar W access path), groups of 5, blocks of 5."""
+    cfg = I.CONFIGS["q_proj_4096x4096_int4_g128"].with_(rows=33, cols=125, tokens=700, group=5,
+                                                       block=5, act_order=act)
+    W = I.weight(cfg)
+    store = [I.x_chunk_storage(cfg, 0, 700)]
+    g = gpu_layer(cfg, W, store)
+    o, H, diag = oracle_layer(cfg, W.astype(np.float64), [I.bf16_to_f32(store[0])])
+    rep = classify_codes(g.q[:, o.perm], o.sweep, "affine", 5)
+    assert_codes(rep)
+    assert rel_fro(g.U, o.U) <= 1e-4
+    e_gpu = O.reconstruction_error(W, g.W_hat, H)
+    e_or = O.reconstruction_error(W, o.what, H)
+    assert abs(e_gpu - e_or) <= 0.01 * e_or
