@@ -150,10 +150,14 @@ __global__ void __launch_bounds__(256)
 // Factor the diagonal block A[k0:k0+m, k0:k0+m] = L11 L11^T and invert L11,
 // in LDS, with 32 x 32 leaves:
 //   for each leaf s (columns o = 32 s .. o + 31):
-//     one wavefront factors the leaf and inverts it in registers (lane i
-//     holds leaf row i; column values are broadcast with readlane);
+//     one wavefront factors and inverts the leaf in registers (lanes 0..31
+//     hold the factor's rows, lanes 32..63 the inverse's columns; column
+//     values of the factor are broadcast with readlane);
 //     the panel below the leaf is solved against the leaf inverse and the
-//     trailing part of the block is updated, as 32 x 32 fp32-MFMA tiles;
+//     trailing part of the block is updated, as 32 x 32 fp32-MFMA tiles.
+//     The wavefront that factors the next leaf first updates that leaf's own
+//     diagonal tile, then factors it while the other wavefronts finish the
+//     rest of the trailing update;
 //   then L11^-1 is assembled from the leaf inverses: X_ba = -X_bb L_ba X_aa,
 //   first for 32-pairs, then for the two 64-halves.
 // The block is padded with an identity to 128 when m < 128.  X (lower) and
@@ -161,16 +165,19 @@ __global__ void __launch_bounds__(256)
 // and finite sets *flag.
 constexpr int kDP = 130;            // LDS pitch (floats): conflict-light MFMA reads
 constexpr int kDiagThreads = 256;   // 4 wavefronts
+constexpr size_t kDiagLds = size_t(2) * 128 * kDP * sizeof(float);  // dynamic part
 
 __device__ __forceinline__ float rl(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// acc += A(32 x K) * B(K x 32) with A(m,k) = a(m,k), B(k,n) = b(k,n), K even.
-template <typename FA, typename FB>
-__device__ __forceinline__ void mma32(f32x16_t &acc, int k0, int k1, int lane, FA a, FB b) {
+// acc += A(32 x K) * B(K x 32) over k in [k0, k1), A(m,k) = a(m,k), B(k,n) = b(k,n).
+template <int k0, int k1, typename FA, typename FB>
+__device__ __forceinline__ void mma32(f32x16_t &acc, int lane, FA a, FB b) {
+#pragma unroll
   for (int kk = k0; kk < k1; kk += 2) {
     const int k = kk + (lane >> 5);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a(lane & 31, k), b(k, lane & 31), acc, 0, 0, 0);
@@ -185,103 +192,141 @@ __device__ __forceinline__ void for_acc(const f32x16_t &acc, int lane, F f) {
   for (int v = 0; v < 16; ++v) f(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), lane & 31, acc[v]);
 }
 
+// One wavefront: factor leaf s of the block in L (lower, in place) and write
+// its inverse into X.  Lanes 0..31 hold the rows of the leaf; lanes 32..63
+// hold the columns of the identity, which become the columns of L^-1.  Step j
+// broadcasts column j of the factor with readlane, and one instruction
+// stream serves both halves: r_k -= r_j l_kj is the right-looking factor
+// update in the lower half and the right-looking inverse update (forward
+// substitution by columns) in the upper half, after r_j *= 1/l_jj.
+// Nothing selects on the lane index inside the steps: per-lane masks would
+// be hoisted out of the leaf loop by the compiler and spill.
+__device__ __forceinline__ void leaf_factor_inverse(float *L, float *X, int o, int lane,
+                                                    unsigned &bad) {
+  const int i = lane & 31;
+  const bool inv_half = lane >= 32;
+  const unsigned onehot = 1u << i;
+  float r[32];
+  // the block's upper part in LDS is zero, so the leaf row loads unmasked
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const float lv = L[(o + i) * kDP + o + k];
+    r[k] = inv_half ? (float)((onehot >> k) & 1u) : lv;
+  }
+  // Entries of the lower half above the diagonal (k > i) take part
+  // unmasked: they stay finite and are never read.
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float piv = rl(r[j], j);
+    // 0 < piv < inf (NaN fails too), tested on the wave-uniform bit pattern
+    // so the test stays in scalar registers
+    const bool ok = (__float_as_uint(piv) - 1u) < 0x7f7fffffu;
+    bad |= ok ? 0u : 1u;
+    // lower half: l_ij (lane j itself gets piv / l_jj = l_jj);
+    // upper half: column j of the inverse is final
+    r[j] *= __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(ok ? piv : 1.f));
+    float lk[32];
+#pragma unroll
+    for (int k = j + 1; k < 32; ++k) lk[k] = rl(r[j], k);
+#pragma unroll
+    for (int k = j + 1; k < 32; ++k) r[k] = fmaf(-r[j], lk[k], r[k]);
+    // finish step j here: deferring its updates to where each column is
+    // next used would keep many broadcast values alive at once in scalar
+    // registers, which then spill
+#pragma unroll
+    for (int k = j + 1; k < 32; ++k) asm volatile("" : "+v"(r[k]));
+  }
+  if (!inv_half) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) L[(o + i) * kDP + o + k] = r[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) X[(o + k) * kDP + o + i] = r[k];
+  }
+}
+
 __global__ void __launch_bounds__(kDiagThreads)
     potrf_inv_block_kernel(float *__restrict__ A, int64_t d, int64_t k0, int m,
                            int *__restrict__ flag) {
   extern __shared__ float sm[];
-  float *L = sm;              // 128 x kDP: the block, factored in place (lower)
-  float *X = sm + 128 * kDP;  // 128 x kDP: the inverse (lower)
+  float *L = sm;                // 128 x kDP: the block, factored in place (lower)
+  float *X = L + 128 * kDP;     // 128 x kDP: the inverse (lower; each part written before read)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float *Ab = A + k0 * d + k0;
-  // 64 elements per thread, loads issued 16 at a time so their latencies overlap
-  for (int t0 = 0; t0 < 64; t0 += 16) {
-    float v[16];
+  const float *Ab = A + k0 * d + k0;
+  // float4 rows when the block is full and rows are 16-byte aligned
+  const bool vec = m == 128 && (d & 3) == 0;
+  if (vec) {
+    f32x4_t v[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const int e = tid + kDiagThreads * (t0 + t);
-      const int i = e >> 7, j = e & 127;
-      // unconditional load from a clamped (valid) address, select afterwards:
-      // no branch, so the 16 loads stay in flight together
-      const float g = Ab[int64_t(min(i, m - 1)) * d + min(j, m - 1)];
-      v[t] = (i < m && j <= i) ? g : (i == j && i >= m ? 1.f : 0.f);
+      const int e = tid + kDiagThreads * t;
+      v[t] = *reinterpret_cast<const f32x4_t *>(Ab + (e >> 5) * int(d) + (e & 31) * 4);
     }
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const int e = tid + kDiagThreads * (t0 + t);
+      const int e = tid + kDiagThreads * t;
+      const int i = e >> 5, j = (e & 31) * 4;
+      float2 lo, hi;
+      lo.x = j <= i ? v[t][0] : 0.f;
+      lo.y = j + 1 <= i ? v[t][1] : 0.f;
+      hi.x = j + 2 <= i ? v[t][2] : 0.f;
+      hi.y = j + 3 <= i ? v[t][3] : 0.f;
+      *reinterpret_cast<float2 *>(L + i * kDP + j) = lo;
+      *reinterpret_cast<float2 *>(L + i * kDP + j + 2) = hi;
+    }
+  } else {
+    // all 64 elements per thread in flight at once; unconditional loads from
+    // clamped (valid) offsets, selected afterwards
+    float v[64];
+#pragma unroll
+    for (int t = 0; t < 64; ++t) {
+      const int e = tid + kDiagThreads * t;
       const int i = e >> 7, j = e & 127;
-      L[i * kDP + j] = v[t];
-      X[i * kDP + j] = 0.f;
+      v[t] = Ab[int(min(i, m - 1)) * int(d) + min(j, m - 1)];
+    }
+#pragma unroll
+    for (int t = 0; t < 64; ++t) {
+      const int e = tid + kDiagThreads * t;
+      const int i = e >> 7, j = e & 127;
+      L[i * kDP + j] = (i < m && j <= i) ? v[t] : (i == j && i >= m ? 1.f : 0.f);
     }
   }
   __syncthreads();
 
-  bool bad = false;
+  unsigned bad = 0;
   for (int s = 0; s < 4; ++s) {
     const int o = 32 * s;
-    if (wave == 0) {
-      const int i = lane & 31;
-      float a[32];
-#pragma unroll
-      for (int k = 0; k < 32; ++k) a[k] = (lane < 32 && k <= i) ? L[(o + i) * kDP + o + k] : 0.f;
-      // leaf factor: column j scaled by 1/l_jj, then rank-1 update of the
-      // rest.  Entries above the diagonal (k > i) take part unmasked: they
-      // stay finite, are never read by the lower part, and are written as 0.
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const float piv = rl(a[j], j);
-        const bool ok = piv > 0.f && piv <= 3.402823466e38f;
-        bad = bad || !ok;
-        const float ljj = ok ? __builtin_amdgcn_sqrtf(piv) : 1.f;
-        a[j] = (i == j) ? ljj : a[j] * __builtin_amdgcn_rcpf(ljj);
-#pragma unroll
-        for (int k = j + 1; k < 32; ++k) a[k] = fmaf(-a[j], rl(a[j], k), a[k]);
-      }
-      // leaf inverse: lane c computes column c by forward substitution
-      float x[32];
-#pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        float acc0 = (r == i) ? 1.f : 0.f, acc1 = 0.f;
-#pragma unroll
-        for (int k = 0; k + 1 < r; k += 2) {
-          acc0 = fmaf(-rl(a[k], r), x[k], acc0);
-          acc1 = fmaf(-rl(a[k + 1], r), x[k + 1], acc1);
-        }
-        if (r & 1) acc0 = fmaf(-rl(a[r - 1], r), x[r - 1], acc0);
-        x[r] = (acc0 + acc1) * __builtin_amdgcn_rcpf(rl(a[r], r));
-      }
-      if (lane < 32) {
-#pragma unroll
-        for (int k = 0; k < 32; ++k) L[(o + i) * kDP + o + k] = k <= i ? a[k] : 0.f;
-#pragma unroll
-        for (int r = 0; r < 32; ++r) X[(o + r) * kDP + o + i] = x[r];
-      }
-    }
+    // leaf s (its diagonal tile was finished by wave 0 itself)
+    if (wave == 0) leaf_factor_inverse(L, X, o, lane, bad);
     __syncthreads();
+    if (s == 3) break;
     const int nb = 3 - s;  // 32-row blocks below the leaf
     // panel: P_b = L[rows of b, leaf cols] * Xleaf^T
     if (wave < nb) {
       const int r0 = o + 32 + 32 * wave;
       f32x16_t acc = {};
-      mma32(acc, 0, 32, lane, [&](int mm, int k) { return L[(r0 + mm) * kDP + o + k]; },
+      mma32<0, 32>(acc, lane, [&](int mm, int k) { return L[(r0 + mm) * kDP + o + k]; },
             [&](int k, int n) { return X[(o + n) * kDP + o + k]; });
       for_acc(acc, lane, [&](int r, int c, float v) { L[(r0 + r) * kDP + o + c] = v; });
     }
     __syncthreads();
-    // trailing part of the block: L[bi][bj] -= P_bi P_bj^T, bj <= bi
+    // trailing part of the block: L[bi][bj] -= P_bi P_bj^T, bj <= bi.  Wave 0
+    // takes tile (0,0), the next leaf's diagonal tile, and goes on to factor
+    // that leaf; waves 1..3 share the other tiles.  The barrier after the
+    // next leaf orders all of them before the next panel solve.
     const int nblk = nb * (nb + 1) / 2;
-    for (int t = wave; t < nblk; t += 4) {
+    for (int t = (wave == 0 ? 0 : wave); t < nblk; t += (wave == 0 ? nblk : 3)) {
       int bi = 0;
       while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
       const int bj = t - bi * (bi + 1) / 2;
       const int ri = o + 32 + 32 * bi, rj = o + 32 + 32 * bj;
       f32x16_t acc = {};
-      mma32(acc, 0, 32, lane, [&](int mm, int k) { return L[(ri + mm) * kDP + o + k]; },
+      mma32<0, 32>(acc, lane, [&](int mm, int k) { return L[(ri + mm) * kDP + o + k]; },
             [&](int k, int n) { return L[(rj + n) * kDP + o + k]; });
       for_acc(acc, lane, [&](int r, int c, float v) {
         if (bi != bj || r >= c) L[(ri + r) * kDP + rj + c] -= v;
       });
     }
-    __syncthreads();
   }
 
   // ---- assemble L^-1 from the leaf inverses; scratch T lives in L's unused
@@ -291,11 +336,11 @@ __global__ void __launch_bounds__(kDiagThreads)
     const int a0 = 64 * wave, b0 = a0 + 32;
     float *T = L + a0 * kDP + b0;  // rows a0.., cols b0.. (above the diagonal)
     f32x16_t acc = {};
-    mma32(acc, 0, 32, lane, [&](int mm, int k) { return L[(b0 + mm) * kDP + a0 + k]; },
+    mma32<0, 32>(acc, lane, [&](int mm, int k) { return L[(b0 + mm) * kDP + a0 + k]; },
           [&](int k, int n) { return X[(a0 + k) * kDP + a0 + n]; });
     for_acc(acc, lane, [&](int r, int c, float v) { T[r * kDP + c] = v; });
     f32x16_t acc2 = {};
-    mma32(acc2, 0, 32, lane, [&](int mm, int k) { return X[(b0 + mm) * kDP + b0 + k]; },
+    mma32<0, 32>(acc2, lane, [&](int mm, int k) { return X[(b0 + mm) * kDP + b0 + k]; },
           [&](int k, int n) { return T[k * kDP + n]; });
     for_acc(acc2, lane, [&](int r, int c, float v) { X[(b0 + r) * kDP + a0 + c] = -v; });
   }
@@ -306,25 +351,45 @@ __global__ void __launch_bounds__(kDiagThreads)
     const int bi = wave >> 1, bj = wave & 1;
     f32x16_t acc = {};
     // X[:64,:64] is lower in 32-blocks: block (kb, bj) is zero for kb < bj
-    mma32(acc, 32 * bj, 64, lane, [&](int mm, int k) { return L[(64 + 32 * bi + mm) * kDP + k]; },
-          [&](int k, int n) { return X[k * kDP + 32 * bj + n]; });
+    auto la = [&](int mm, int k) { return L[(64 + 32 * bi + mm) * kDP + k]; };
+    auto xb = [&](int k, int n) { return X[k * kDP + 32 * bj + n]; };
+    mma32<32, 64>(acc, lane, la, xb);
+    if (bj == 0) mma32<0, 32>(acc, lane, la, xb);
     __syncthreads();
     for_acc(acc, lane, [&](int r, int c, float v) { T[(32 * bi + r) * kDP + 32 * bj + c] = v; });
     __syncthreads();
     f32x16_t acc2 = {};
     // X[64:,64:] is lower in 32-blocks: block (bi, kb) is zero for kb > bi
-    mma32(acc2, 0, 32 * (bi + 1), lane,
-          [&](int mm, int k) { return X[(64 + 32 * bi + mm) * kDP + 64 + k]; },
-          [&](int k, int n) { return T[k * kDP + 32 * bj + n]; });
+    auto xa = [&](int mm, int k) { return X[(64 + 32 * bi + mm) * kDP + 64 + k]; };
+    auto tb = [&](int k, int n) { return T[k * kDP + 32 * bj + n]; };
+    mma32<0, 32>(acc2, lane, xa, tb);
+    if (bi == 1) mma32<32, 64>(acc2, lane, xa, tb);
     for_acc(acc2, lane, [&](int r, int c, float v) { X[(64 + 32 * bi + r) * kDP + 32 * bj + c] = -v; });
   }
   __syncthreads();
   if (tid == 0 && bad) *flag = 1;
+  float *Aw = A + k0 * d + k0;
+  if (vec) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int e = tid + kDiagThreads * t;
+      const int i = e >> 5, j = (e & 31) * 4;
+      const float2 lo = *reinterpret_cast<const float2 *>(X + i * kDP + j);
+      const float2 hi = *reinterpret_cast<const float2 *>(X + i * kDP + j + 2);
+      f32x4_t w;
+      w[0] = j <= i ? lo.x : 0.f;
+      w[1] = j + 1 <= i ? lo.y : 0.f;
+      w[2] = j + 2 <= i ? hi.x : 0.f;
+      w[3] = j + 3 <= i ? hi.y : 0.f;
+      *reinterpret_cast<f32x4_t *>(Aw + i * int(d) + j) = w;
+    }
+  } else {
 #pragma unroll 16
-  for (int t = 0; t < 64; ++t) {
-    const int e = tid + kDiagThreads * t;
-    const int i = e >> 7, j = e & 127;
-    if (i < m && j < m) Ab[int64_t(i) * d + j] = j <= i ? X[i * kDP + j] : 0.f;
+    for (int t = 0; t < 64; ++t) {
+      const int e = tid + kDiagThreads * t;
+      const int i = e >> 7, j = e & 127;
+      if (i < m && j < m) Aw[int64_t(i) * d + j] = j <= i ? X[i * kDP + j] : 0.f;
+    }
   }
 }
 
@@ -369,7 +434,7 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
                   d, (const int32_t *)perm, (const uint8_t *)dead, (const double *)delta, A));
 
   // ---- blocked Cholesky A = L L^T; diagonal blocks end up holding L_ii^-1
-  const size_t lds = size_t(2) * 128 * kDP * sizeof(float);
+  const size_t lds = kDiagLds;
   if (!g_lds_set) {
     hipError_t e = hipFuncSetAttribute((const void *)potrf_inv_block_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
