@@ -10,7 +10,8 @@
 // d^3/3 of an explicit inverse followed by a second factorization.
 //
 // Workspace layout: A (d x d float) | T (scratch of the inverse products) |
-// flag (int) and delta (double).
+// flag (int) and delta (double) | rank (int32 x d).  The symmetric copy of H
+// that the permuting gather reads is staged in the output U.
 #include <algorithm>
 #include <vector>
 
@@ -57,16 +58,19 @@ int64_t tree_scratch(int64_t d, std::vector<Node> *nodes_out, int *hmax_out) {
 }
 
 // ---------------------------------------------------------------- kernels
-// dead flags, damping delta = percdamp * mean(diag with dead -> 1), flag := 0.
+// dead flags, damping delta = percdamp * mean(diag with dead -> 1), flag := 0,
+// rank := 0.
 __global__ void __launch_bounds__(1024)
     diag_prep_kernel(const double *__restrict__ hdiag, int64_t d, double percdamp,
-                     uint8_t *__restrict__ dead, double *__restrict__ delta, int *__restrict__ flag) {
+                     uint8_t *__restrict__ dead, double *__restrict__ delta, int *__restrict__ flag,
+                     int32_t *__restrict__ rank) {
   __shared__ double red[1024];
   double s = 0.0;
   for (int64_t i = threadIdx.x; i < d; i += 1024) {
     const double v = hdiag[i];
     const bool z = v == 0.0;
     dead[i] = z ? 1 : 0;
+    rank[i] = 0;
     s += z ? 1.0 : v;
   }
   red[threadIdx.x] = s;
@@ -81,68 +85,116 @@ __global__ void __launch_bounds__(1024)
   }
 }
 
-// perm[rank(i)] = i, rank by decreasing hdiag, ties by lower index (stable).
+// Processing position of column i: the number of columns ahead of it by
+// decreasing hdiag, ties to the lower index (a stable sort).  The j range is
+// split over gridDim.y slices whose counts are added atomically.  NaN keys
+// (only from non-finite inputs) are ordered as -inf so that the ranks always
+// form a permutation.
+constexpr int kRankSplit = 16;
 __global__ void __launch_bounds__(256)
-    rank_perm_kernel(const double *__restrict__ hdiag, int64_t d, int act_order,
-                     int32_t *__restrict__ perm) {
+    rank_count_kernel(const double *__restrict__ hdiag, int64_t d, int32_t *__restrict__ rank) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (!act_order) {
-    if (i < d) perm[i] = (int32_t)i;
-    return;
-  }
+  const int64_t per = (d + gridDim.y - 1) / gridDim.y;
+  const int64_t j0 = int64_t(blockIdx.y) * per, j1 = min(d, j0 + per);
   __shared__ double keys[256];
-  // NaN keys (only from non-finite inputs) are ordered as -inf so that the
-  // ranks always form a permutation.
   auto key = [](double v) { return v == v ? v : -INFINITY; };
   const double ki = i < d ? key(hdiag[i]) : 0.0;
-  int64_t rank = 0;
-  for (int64_t j0 = 0; j0 < d; j0 += 256) {
+  int cnt = 0;
+  for (int64_t c0 = j0; c0 < j1; c0 += 256) {
     __syncthreads();
-    const int64_t j = j0 + threadIdx.x;
-    keys[threadIdx.x] = j < d ? key(hdiag[j]) : 0.0;
+    const int64_t j = c0 + threadIdx.x;
+    keys[threadIdx.x] = j < j1 ? key(hdiag[j]) : 0.0;
     __syncthreads();
-    const int lim = (d - j0) < 256 ? (int)(d - j0) : 256;
+    const int lim = (j1 - c0) < 256 ? (int)(j1 - c0) : 256;
+#pragma unroll 8
     for (int t = 0; t < lim; ++t) {
       const double kj = keys[t];
-      const int64_t jj = j0 + t;
-      rank += (kj > ki) || (kj == ki && jj < i);
+      cnt += (kj > ki) || (kj == ki && c0 + t < i);
     }
   }
-  if (i < d) perm[rank] = (int32_t)i;
+  if (i < d && cnt) atomicAdd(rank + i, cnt);
 }
 
-// A[a][b] = Hp[d-1-a][d-1-b] on and below the diagonal, 0 above, where
-// Hp[x][y] = H[perm[x]][perm[y]] (upper triangle of H read), dead diagonal
-// entries taken as 1, and delta added on the diagonal.
+// perm[rank[i]] = i (identity without act-order).
 __global__ void __launch_bounds__(256)
-    gather_reversed_kernel(const float *__restrict__ H, int64_t d, const int32_t *__restrict__ perm,
-                           const uint8_t *__restrict__ dead, const double *__restrict__ delta,
-                           float *__restrict__ A) {
-  const int64_t a0 = int64_t(blockIdx.y) * 64, b0 = int64_t(blockIdx.x) * 64;
-  __shared__ int32_t qa[64], qb[64];
-  if (threadIdx.x < 64) {
-    const int64_t a = a0 + threadIdx.x;
-    qa[threadIdx.x] = a < d ? min(max(perm[d - 1 - a], 0), (int32_t)(d - 1)) : 0;
-  } else if (threadIdx.x < 128) {
-    const int64_t b = b0 + threadIdx.x - 64;
-    qb[threadIdx.x - 64] = b < d ? min(max(perm[d - 1 - b], 0), (int32_t)(d - 1)) : 0;
+    rank_scatter_kernel(const int32_t *__restrict__ rank, int64_t d, int act_order,
+                        int32_t *__restrict__ perm) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= d) return;
+  if (!act_order) {
+    perm[i] = (int32_t)i;
+    return;
+  }
+  const int32_t r = rank[i];
+  if (r >= 0 && r < d) perm[r] = (int32_t)i;
+}
+
+// S = H with its lower triangle filled from the upper one, by 64 x 64 tiles:
+// upper tile (ti, tj) is read once and written to (ti, tj) and, transposed,
+// to (tj, ti).  Reads and writes are row-contiguous.
+__global__ void __launch_bounds__(256)
+    symmetrize_kernel(const float *__restrict__ H, int64_t d, float *__restrict__ S) {
+  const int ti = blockIdx.y, tj = blockIdx.x;
+  if (ti > tj) return;
+  __shared__ float t[64][65];
+  const int c = threadIdx.x & 63, r0 = threadIdx.x >> 6;
+  const int64_t I0 = int64_t(ti) * 64, J0 = int64_t(tj) * 64;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = r0 + 4 * k;
+    const int64_t gr = I0 + r, gc = J0 + c;
+    t[r][c] = (gr < d && gc < d) ? H[gr * d + gc] : 0.f;
   }
   __syncthreads();
-  const double dl = *delta;
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int ra = e >> 6, cb = e & 63;
-    const int64_t a = a0 + ra, b = b0 + cb;
-    if (a >= d || b >= d) continue;
-    float v = 0.f;
-    if (a > b) {
-      const int64_t x = qa[ra], y = qb[cb];
-      v = x < y ? H[x * d + y] : H[y * d + x];
-    } else if (a == b) {
-      const int64_t x = qa[ra];
-      const double h = dead[x] ? 1.0 : (double)H[x * d + x];
-      v = (float)(h + dl);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = r0 + 4 * k;
+    const int64_t gr = I0 + r, gc = J0 + c;
+    if (gr < d && gc < d) S[gr * d + gc] = (ti == tj && c < r) ? t[c][r] : t[r][c];
+  }
+  if (ti != tj) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = r0 + 4 * k;
+      const int64_t gr = J0 + r, gc = I0 + c;
+      if (gr < d && gc < d) S[gr * d + gc] = t[c][r];
     }
-    A[a * d + b] = v;
+  }
+}
+
+// Row a of A, on and below the diagonal: A[a][b] = Hp[d-1-a][d-1-b] with
+// Hp[x][y] = S[perm[x]][perm[y]] (S the symmetric H), dead diagonal entries
+// taken as 1 and delta added on the diagonal.  One workgroup per row: the
+// source row of S is read contiguously (into LDS when kLds), then gathered by
+// the permutation; the output row is written contiguously.  A's strict upper
+// triangle is not written (nothing reads it).
+template <bool kLds>
+__global__ void __launch_bounds__(256)
+    gather_rows_kernel(const float *__restrict__ S, int64_t d, const int32_t *__restrict__ perm,
+                       const uint8_t *__restrict__ dead, const double *__restrict__ delta,
+                       float *__restrict__ A) {
+  extern __shared__ float srow[];
+  const double dl = *delta;
+  for (int64_t a = blockIdx.x; a < d; a += gridDim.x) {
+    const int64_t x = min(max(perm[d - 1 - a], 0), (int32_t)(d - 1));
+    const float *src = S + x * d;
+    if (kLds) {
+      __syncthreads();
+#pragma unroll 8
+      for (int64_t c = threadIdx.x; c < d; c += 256) srow[c] = src[c];
+      __syncthreads();
+    }
+#pragma unroll 8
+    for (int64_t b = threadIdx.x; b <= a; b += 256) {
+      float v;
+      if (b == a) {
+        v = (float)((dead[x] ? 1.0 : (double)(kLds ? srow[x] : src[x])) + dl);
+      } else {
+        const int64_t y = min(max(perm[d - 1 - b], 0), (int32_t)(d - 1));
+        v = kLds ? srow[y] : src[y];
+      }
+      A[a * d + b] = v;
+    }
   }
 }
 
@@ -402,13 +454,15 @@ __global__ void __launch_bounds__(256)
 }
 
 bool g_lds_set = false;
+bool g_rows_lds_set = false;
+constexpr size_t kMaxRowLds = 160 * 1024;
 
 }  // namespace
 
 size_t prepare_ws_bytes(int64_t d) {
   const size_t a = align256(size_t(d) * size_t(d) * sizeof(float));
   const size_t t = align256(size_t(tree_scratch(d, nullptr, nullptr)) * sizeof(float));
-  return a + t + 256;
+  return a + t + 256 + align256(size_t(d) * sizeof(int32_t));
 }
 
 gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
@@ -424,14 +478,39 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
   uint8_t *tail = base + align256(size_t(d) * size_t(d) * 4) + align256(size_t(tsz) * 4);
   int *flag = reinterpret_cast<int *>(tail);
   double *delta = reinterpret_cast<double *>(tail + 8);
+  int32_t *rank = reinterpret_cast<int32_t *>(tail + 256);
 
   GPTQ_TRY(launch("prep_diag", diag_prep_kernel, dim3(1), dim3(1024), 0, stream, hdiag, d,
-                  (double)p.percdamp, dead, delta, flag));
-  GPTQ_TRY(launch("prep_rank_perm", rank_perm_kernel, dim3((unsigned)cdiv(d, 256)), dim3(256), 0,
-                  stream, hdiag, d, (int)p.act_order, perm));
+                  (double)p.percdamp, dead, delta, flag, rank));
+  if (p.act_order)
+    GPTQ_TRY(launch("prep_rank_perm", rank_count_kernel,
+                    dim3((unsigned)cdiv(d, 256), (unsigned)std::min<int64_t>(kRankSplit, d)),
+                    dim3(256), 0, stream, hdiag, d, rank));
+  GPTQ_TRY(launch("prep_rank_perm", rank_scatter_kernel, dim3((unsigned)cdiv(d, 256)), dim3(256), 0,
+                  stream, (const int32_t *)rank, d, (int)p.act_order, perm));
+  // the symmetric H is staged in U's memory (U is written last)
   const unsigned g64 = (unsigned)cdiv(d, 64);
-  GPTQ_TRY(launch("prep_gather", gather_reversed_kernel, dim3(g64, g64), dim3(256), 0, stream, H,
-                  d, (const int32_t *)perm, (const uint8_t *)dead, (const double *)delta, A));
+  GPTQ_TRY(launch("prep_symmetrize", symmetrize_kernel, dim3(g64, g64), dim3(256), 0, stream, H, d,
+                  U));
+  const unsigned growsn = (unsigned)std::min<int64_t>(d, 65535);
+  const size_t srow_bytes = size_t(d) * sizeof(float);
+  if (srow_bytes <= kMaxRowLds) {
+    if (srow_bytes > 65536 && !g_rows_lds_set) {
+      hipError_t e = hipFuncSetAttribute((const void *)gather_rows_kernel<true>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)kMaxRowLds);
+      if (e != hipSuccess)
+        return fail(GPTQ_ERR_DEVICE, std::string("cannot raise LDS limit: ") + hipGetErrorString(e));
+      g_rows_lds_set = true;
+    }
+    GPTQ_TRY(launch("prep_gather", gather_rows_kernel<true>, dim3(growsn), dim3(256), srow_bytes,
+                    stream, (const float *)U, d, (const int32_t *)perm, (const uint8_t *)dead,
+                    (const double *)delta, A));
+  } else {
+    GPTQ_TRY(launch("prep_gather", gather_rows_kernel<false>, dim3(growsn), dim3(256), 0, stream,
+                    (const float *)U, d, (const int32_t *)perm, (const uint8_t *)dead,
+                    (const double *)delta, A));
+  }
 
   // ---- blocked Cholesky A = L L^T; diagonal blocks end up holding L_ii^-1
   const size_t lds = kDiagLds;

@@ -428,6 +428,49 @@ __global__ void __launch_bounds__(256)
     }
 }
 
+// Row-staged forms of the two kernels above: one workgroup per row, the
+// source row read contiguously into LDS, permuted there, and the output row
+// written contiguously (the plain forms gather or scatter single elements
+// straight from and to memory).
+__global__ void __launch_bounds__(256)
+    gather_cols_lds_kernel(const float *__restrict__ W, int64_t rows, int64_t cols,
+                           const int32_t *__restrict__ perm, const uint8_t *__restrict__ dead,
+                           float *__restrict__ Wp) {
+  extern __shared__ float srow[];
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    __syncthreads();
+#pragma unroll 8
+    for (int64_t c = threadIdx.x; c < cols; c += 256) srow[c] = dead[c] ? 0.f : W[r * cols + c];
+    __syncthreads();
+#pragma unroll 8
+    for (int64_t p = threadIdx.x; p < cols; p += 256)
+      Wp[r * cols + p] = srow[min(max(perm[p], 0), (int32_t)(cols - 1))];
+  }
+}
+
+__global__ void __launch_bounds__(256)
+    scatter_cols_lds_kernel(const float *__restrict__ Wp, const uint8_t *__restrict__ qp,
+                            int64_t rows, int64_t cols, const int32_t *__restrict__ perm,
+                            float *__restrict__ W, uint8_t *__restrict__ q) {
+  extern __shared__ float srow[];
+  uint8_t *qrow = reinterpret_cast<uint8_t *>(srow + cols);
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    __syncthreads();
+#pragma unroll 8
+    for (int64_t p = threadIdx.x; p < cols; p += 256) {
+      const int32_t c = min(max(perm[p], 0), (int32_t)(cols - 1));
+      srow[c] = Wp[r * cols + p];
+      qrow[c] = qp[r * cols + p];
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int64_t c = threadIdx.x; c < cols; c += 256) {
+      W[r * cols + c] = srow[c];
+      q[r * cols + c] = qrow[c];
+    }
+  }
+}
+
 // W[r][perm[p]] = Wp[r][p], q[r][perm[p]] = qp[r][p]
 __global__ void __launch_bounds__(256)
     scatter_cols_kernel(const float *__restrict__ Wp, const uint8_t *__restrict__ qp, int64_t rows,
@@ -484,12 +527,20 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   uint8_t *qp = q;
   const unsigned gx = (unsigned)std::min<int64_t>(cdiv(cols, 256), 64);
   const unsigned gy = (unsigned)std::min<int64_t>(rows, 16384);
+  // LDS of the row-staged gather/scatter (a float and a code per column);
+  // wider rows take the plain kernels
+  const size_t row_lds = size_t(cols) * 5;
+  const unsigned growsn = (unsigned)std::min<int64_t>(rows, 65535);
   if (p.act_order) {
     Wp = reinterpret_cast<float *>(base);
     base += align256(size_t(rows) * size_t(cols) * sizeof(float));
     qp = base;
-    GPTQ_TRY(launch("quant_gather", gather_cols_kernel, dim3(gx, gy), dim3(256), 0, stream,
-                    (const float *)W, rows, cols, perm, dead, Wp));
+    if (row_lds <= 65536)
+      GPTQ_TRY(launch("quant_gather", gather_cols_lds_kernel, dim3(growsn), dim3(256),
+                      size_t(cols) * 4, stream, (const float *)W, rows, cols, perm, dead, Wp));
+    else
+      GPTQ_TRY(launch("quant_gather", gather_cols_kernel, dim3(gx, gy), dim3(256), 0, stream,
+                      (const float *)W, rows, cols, perm, dead, Wp));
   } else {
     GPTQ_TRY(launch("quant_zero_dead", zero_dead_kernel, dim3(gx, gy), dim3(256), 0, stream,
                     W, rows, cols, dead));
@@ -547,8 +598,14 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   }
 
   if (p.act_order)
-    GPTQ_TRY(launch("quant_scatter", scatter_cols_kernel, dim3(gx, gy), dim3(256), 0, stream,
-                    (const float *)Wp, (const uint8_t *)qp, rows, cols, perm, W, q));
+  {
+    if (row_lds <= 65536)
+      GPTQ_TRY(launch("quant_scatter", scatter_cols_lds_kernel, dim3(growsn), dim3(256), row_lds,
+                      stream, (const float *)Wp, (const uint8_t *)qp, rows, cols, perm, W, q));
+    else
+      GPTQ_TRY(launch("quant_scatter", scatter_cols_kernel, dim3(gx, gy), dim3(256), 0, stream,
+                      (const float *)Wp, (const uint8_t *)qp, rows, cols, perm, W, q));
+  }
   const int gsz = q4k ? 32 : p.group;
   GPTQ_TRY(launch("quant_g_idx", g_idx_kernel, dim3((unsigned)cdiv(cols, 256)), dim3(256), 0, stream,
                   perm, cols, gsz, g_idx));
