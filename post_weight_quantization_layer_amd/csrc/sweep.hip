@@ -4,14 +4,17 @@
 // gguf q4_k quantization", summary).
 //
 // For each block of B <= 128 columns (processing order):
-//   sweep kernel    one wavefront per row; lane l holds the row's block
-//                   columns l and l+64 in registers; the B x B block of U sits
-//                   in LDS.  Step j broadcasts w_j (readlane), quantizes it,
+//   sweep kernel    a wavefront holds 4 rows of the block in registers, 16
+//                   lanes per row and 8 columns per lane; the B x B block of
+//                   U and the reciprocals of its diagonal sit in LDS.  Step j
+//                   broadcasts w_j within the row's lanes, quantizes it,
 //                   forms e_j = (w_j - q(w_j)) / U_jj and updates the lanes'
 //                   later columns with -e_j U_jk.  Group grids are chosen at a
-//                   group's first column with wavefront min/max reductions.
+//                   group's first column with 16-lane min/max reductions.
 //                   Writes the block's w^ and codes, and e_j into Err.
-//   trailing GEMM   W[:, i2:] -= Err * U[block, i2:] on fp32 MFMA.
+//   trailing GEMMs  on fp32 MFMA, in two levels: W[:, i2:s2] -= Err_b U[b, i2:s2]
+//                   within the block's super-block [s1, s2), and once per
+//                   super-block W[:, s2:] -= Err_S U[S, s2:] (K = s2 - s1).
 //
 // Grid decisions (scale, zero, code) are taken in fp32 with IEEE division
 // and round-half-to-even (v_rndne_f32), fp16 super-scales with
@@ -24,13 +27,15 @@ namespace gptq {
 namespace {
 
 constexpr int kMaxB = 128;
+constexpr int kMaxSuper = 512;      // columns per far (deferred) trailing update
 constexpr int kSweepThreads = 256;  // 4 wavefronts, 4 rows each at a time
 constexpr int kSweepMaxWG = 512;
 
 struct SweepArgs {
   float *W;        // working weights, row-major, ld = cols (processing order)
   uint8_t *q;      // codes, ld = cols
-  float *Err;      // rows x kMaxB
+  float *Err;      // this block's first column of the error buffer, ld = ldE
+  int ldE;
   const float *U;  // ld = cols
   int64_t rows, cols;
   int i1, B;
@@ -192,6 +197,7 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
   const int64_t rows_per_pass = int64_t(gridDim.x) * (kSweepThreads / 64) * 4;
   // 16-byte W accesses need a 4-float aligned row stride and block start
   const bool vec = (ld & 3) == 0 && (a.i1 & 3) == 0;
+  const bool evec = (a.ldE & 3) == 0 && (reinterpret_cast<uintptr_t>(a.Err) & 15) == 0;
 
   for (int64_t r0 = (int64_t(blockIdx.x) * (kSweepThreads / 64) + wave) * 4; r0 < a.rows;
        r0 += rows_per_pass) {
@@ -384,8 +390,8 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
 
     if (rv) {
       uint8_t *qrow = a.q + row * ld + a.i1;
-      float *erow = a.Err + row * kMaxB;
-      if (c0 + kCPL <= B) {
+      float *erow = a.Err + row * a.ldE;
+      if (evec && c0 + kCPL <= B) {
         *reinterpret_cast<f32x4_t *>(erow + c0) = f32x4_t{e[0], e[1], e[2], e[3]};
         *reinterpret_cast<f32x4_t *>(erow + c0 + 4) = f32x4_t{e[4], e[5], e[6], e[7]};
       } else {
@@ -506,7 +512,7 @@ bool g_sweep_lds_set[4] = {false, false, false, false};
 }  // namespace
 
 size_t quantize_ws_bytes(int64_t rows, int64_t cols, const gptq_params &p) {
-  size_t n = align256(size_t(rows) * kMaxB * sizeof(float));  // Err
+  size_t n = align256(size_t(rows) * kMaxSuper * sizeof(float));  // Err
   if (p.act_order) {
     n += align256(size_t(rows) * size_t(cols) * sizeof(float));  // Wp
     n += align256(size_t(rows) * size_t(cols));                  // qp
@@ -522,7 +528,7 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   (void)ws_bytes;
   uint8_t *base = static_cast<uint8_t *>(ws);
   float *Err = reinterpret_cast<float *>(base);
-  base += align256(size_t(rows) * kMaxB * sizeof(float));
+  base += align256(size_t(rows) * kMaxSuper * sizeof(float));
   float *Wp = W;
   uint8_t *qp = q;
   const unsigned gx = (unsigned)std::min<int64_t>(cdiv(cols, 256), 64);
@@ -566,7 +572,6 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   SweepArgs a{};
   a.W = Wp;
   a.q = qp;
-  a.Err = Err;
   a.U = U;
   a.rows = rows;
   a.cols = cols;
@@ -578,23 +583,48 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   a.Dm = Dm;
   a.sc = sc;
   a.mc = mc;
-  for (int64_t i1 = 0; i1 < cols; i1 += B) {
-    const int Bc = (int)std::min<int64_t>(B, cols - i1);
-    a.i1 = (int)i1;
-    a.B = Bc;
-    const char *nm = q4k ? "sweep_q4k" : "sweep_affine";
-    const dim3 grid(nwg), blk(kSweepThreads);
-    switch (variant) {
-      case 0: GPTQ_TRY(launch(nm, sweep_kernel<0, false>, grid, blk, lds, stream, a)); break;
-      case 1: GPTQ_TRY(launch(nm, sweep_kernel<0, true>, grid, blk, lds, stream, a)); break;
-      case 2: GPTQ_TRY(launch(nm, sweep_kernel<1, false>, grid, blk, lds, stream, a)); break;
-      default: GPTQ_TRY(launch(nm, sweep_kernel<1, true>, grid, blk, lds, stream, a)); break;
+  // Two-level lazy updates: blocks are grouped into super-blocks of m
+  // blocks.  After each block only the rest of its super-block is updated
+  // (K = B); the columns past the super-block get one update from the whole
+  // super-block's errors (K = m B).  A group's grid is chosen from its
+  // columns' current values, so a group must not reach past its super-block
+  // unless it starts with it: the super-block size divides the group size or
+  // is a multiple of it.
+  const int G = q4k ? 256 : p.group;
+  int m = 1;
+  if ((B & 3) == 0)
+    for (int c = kMaxSuper / B; c > 1; --c)
+      if ((G % (c * B)) == 0 || ((c * B) % G) == 0) {
+        m = c;
+        break;
+      }
+  const int SB = m * B;
+  a.ldE = m == 1 ? kMaxB : SB;
+  const char *nm = q4k ? "sweep_q4k" : "sweep_affine";
+  const dim3 grid(nwg), blk(kSweepThreads);
+  for (int64_t s1 = 0; s1 < cols; s1 += SB) {
+    const int64_t s2 = std::min<int64_t>(s1 + SB, cols);
+    for (int64_t i1 = s1; i1 < s2; i1 += B) {
+      const int Bc = (int)std::min<int64_t>(B, s2 - i1);
+      a.i1 = (int)i1;
+      a.B = Bc;
+      a.Err = Err + (i1 - s1);
+      switch (variant) {
+        case 0: GPTQ_TRY(launch(nm, sweep_kernel<0, false>, grid, blk, lds, stream, a)); break;
+        case 1: GPTQ_TRY(launch(nm, sweep_kernel<0, true>, grid, blk, lds, stream, a)); break;
+        case 2: GPTQ_TRY(launch(nm, sweep_kernel<1, false>, grid, blk, lds, stream, a)); break;
+        default: GPTQ_TRY(launch(nm, sweep_kernel<1, true>, grid, blk, lds, stream, a)); break;
+      }
+      const int64_t i2 = i1 + Bc;
+      if (i2 < s2)
+        GPTQ_TRY(gemm_f32(Err + (i1 - s1), a.ldE, U + i1 * cols + i2, cols, Wp + i2, cols,
+                          (int)rows, (int)(s2 - i2), Bc, -1.f, 1.f, 0, 0, 0, 0, stream,
+                          "trailing_near"));
     }
-    const int64_t i2 = i1 + Bc;
-    if (i2 < cols) {
-      GPTQ_TRY(gemm_f32(Err, kMaxB, U + i1 * cols + i2, cols, Wp + i2, cols, (int)rows,
-                        (int)(cols - i2), Bc, -1.f, 1.f, 0, 0, 0, 0, stream, "trailing_gemm"));
-    }
+    if (s2 < cols)
+      GPTQ_TRY(gemm_f32(Err, a.ldE, U + s1 * cols + s2, cols, Wp + s2, cols, (int)rows,
+                        (int)(cols - s2), (int)(s2 - s1), -1.f, 1.f, 0, 0, 0, 0, stream,
+                        "trailing_gemm"));
   }
 
   if (p.act_order)
