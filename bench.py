@@ -206,7 +206,7 @@ def main():
 
     kernels = {}
     names = ["hessian_syrk_bf16", "hessian_syrk_f32", "hessian_diag", "prep_diag",
-             "prep_rank_perm", "prep_symmetrize", "prep_gather", "chol_diag_block", "chol_trsm", "chol_syrk",
+             "prep_rank_perm", "prep_symmetrize", "prep_gather", "chol_diag_block", "chol_trsm", "chol_near", "chol_syrk",
              "trtri_gemm", "prep_rotate", "quant_gather", "quant_zero_dead", "sweep_affine",
              "sweep_q4k", "trailing_near", "trailing_gemm", "quant_scatter", "quant_g_idx", "pack"]
     if not args.no_profile:

@@ -3,7 +3,9 @@
 //
 // U (upper, U^T U = Hp^-1) is reached without forming Hp^-1:
 //   A  = J Hp J            (J the exchange matrix: reversed processing order)
-//   A  = L L^T             (blocked right-looking Cholesky, lower, in place)
+//   A  = L L^T             (blocked right-looking Cholesky, lower, in place;
+//                           128-column diagonal blocks, trailing updates
+//                           deferred per 512-column panel)
 //   U  = J L^-1 J          (recursive triangular inverse, then a rotation)
 // since Hp = (J L J)(J L J)^T with J L J upper, and the upper Cholesky factor
 // of Hp^-1 is unique.  This costs d^3/3 + d^3/3 flops instead of the d^3 +
@@ -21,6 +23,7 @@ namespace gptq {
 namespace {
 
 constexpr int kNB = 128;          // diagonal block of the factorization
+constexpr int64_t kPanel = 512;   // columns per deferred trailing update
 
 struct Node {
   int b0, bm, b1, height;
@@ -521,20 +524,35 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
       return fail(GPTQ_ERR_DEVICE, std::string("cannot raise LDS limit: ") + hipGetErrorString(e));
     g_lds_set = true;
   }
-  for (int64_t k0 = 0; k0 < d; k0 += kNB) {
-    const int m = (int)std::min<int64_t>(kNB, d - k0);
-    GPTQ_TRY(launch("chol_diag_block", potrf_inv_block_kernel, dim3(1), dim3(kDiagThreads), lds,
-                    stream, A, d, k0, m, flag));
-    const int64_t r = d - k0 - m;
-    if (r <= 0) break;
-    float *A21 = A + (k0 + m) * d + k0;
-    // L21 = A21 * L11^-T   (in place: one column tile, each workgroup owns its rows)
-    GPTQ_TRY(gemm_f32(A21, d, A + k0 * d + k0, d, A21, d, (int)r, m, m, 1.f, 0.f, 1, 0, 0, 0,
-                      stream, "chol_trsm"));
-    // A22 -= L21 L21^T (lower triangle)
-    float *A22 = A + (k0 + m) * d + (k0 + m);
-    GPTQ_TRY(gemm_f32(A21, d, A21, d, A22, d, (int)r, (int)r, m, -1.f, 1.f, 1, 1, 0, 0, stream,
-                      "chol_syrk"));
+  // Two levels: the trailing update inside a panel of kPanel columns is
+  // applied after each diagonal block (K = 128), the update of the columns
+  // past the panel once per panel (K = kPanel).
+  for (int64_t c0 = 0; c0 < d; c0 += kPanel) {
+    const int64_t c1 = std::min<int64_t>(c0 + kPanel, d);
+    for (int64_t k0 = c0; k0 < c1; k0 += kNB) {
+      const int m = (int)std::min<int64_t>(kNB, d - k0);
+      GPTQ_TRY(launch("chol_diag_block", potrf_inv_block_kernel, dim3(1), dim3(kDiagThreads), lds,
+                      stream, A, d, k0, m, flag));
+      const int64_t r = d - k0 - m;
+      if (r <= 0) break;
+      float *A21 = A + (k0 + m) * d + k0;
+      // L21 = A21 * L11^-T   (in place: each workgroup owns whole rows)
+      GPTQ_TRY(gemm_f32(A21, d, A + k0 * d + k0, d, A21, d, (int)r, m, m, 1.f, 0.f, 1, 0, 0, 0,
+                        stream, "chol_trsm"));
+      // the rest of the panel: A[k0+m:, k0+m:c1] -= L21 L21[0:c1-k0-m]^T
+      // (the part of it above the diagonal is written too, and never read)
+      const int64_t nn = c1 - (k0 + m);
+      if (nn > 0)
+        GPTQ_TRY(gemm_f32(A21, d, A21, d, A + (k0 + m) * d + (k0 + m), d, (int)r, (int)nn, m,
+                          -1.f, 1.f, 1, 0, 0, 0, stream, "chol_near"));
+    }
+    // the columns past the panel: A22 -= Lp Lp^T (lower triangle), K = c1 - c0
+    const int64_t r2 = d - c1;
+    if (r2 > 0) {
+      const float *Lp = A + c1 * d + c0;
+      GPTQ_TRY(gemm_f32(Lp, d, Lp, d, A + c1 * d + c1, d, (int)r2, (int)r2, (int)(c1 - c0), -1.f,
+                        1.f, 1, 1, 0, 0, stream, "chol_syrk"));
+    }
   }
 
   // ---- recursive triangular inverse, bottom-up by tree height:
