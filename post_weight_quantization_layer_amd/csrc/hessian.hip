@@ -22,8 +22,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 256;       // H tile edge
 constexpr int kBK = 32;          // tokens per pipeline stage
-constexpr int kThreads = 512;    // 8 waves (2 per SIMD), each a 128 x 64 sub-tile
-constexpr int kStages = 4;       // LDS ring depth (3 stages in flight)
+constexpr int kThreads = 256;    // 4 waves (1 per SIMD), each a 128 x 128 sub-tile
+constexpr int kStages = 4;       // LDS ring depth
 constexpr int kRowBytes = kBK * 2;                 // 64 B of one X row per stage
 constexpr int kPanelBytes = kTile * kRowBytes;     // 16 KB per operand per stage
 constexpr int kStageBytes = 2 * kPanelBytes;
@@ -41,17 +41,18 @@ __device__ __forceinline__ void vm_wait() {
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 // Copy one 256-row x 32-token panel of X into LDS with global_load_lds
-// (16 bytes per lane; lane l of an instruction lands at base + 16 l), two
+// (16 bytes per lane; lane l of an instruction lands at base + 16 l), four
 // 1 KB blocks per wave.  Slot s of the panel is row s/4, swizzled position
 // s%4, so each lane fetches the global chunk that belongs at its slot (four
 // lanes cover one row's 64 contiguous bytes).  Rows past d are clamped to
 // row d-1 (they only feed outputs that are never stored).
+constexpr int kCopiesPerPanel = kPanelBytes / 1024 / (kThreads / 64);  // per wave
 __device__ __forceinline__ void issue_panel(const uint16_t *__restrict__ X, int64_t ld, int64_t d,
                                             int64_t row0, int64_t k0, uint8_t *lds, int wave,
                                             int lane) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int blk = wave * 2 + i;
+  for (int i = 0; i < kCopiesPerPanel; ++i) {
+    const int blk = wave * kCopiesPerPanel + i;
     const int slot = blk * 64 + lane;
     const int r = slot >> 2, c = (slot & 3) ^ swz(r);
     const int64_t gr = min(row0 + r, d - 1);
@@ -65,7 +66,7 @@ __device__ __forceinline__ void tail_panel(const uint16_t *__restrict__ X, int64
                                            int64_t n, int64_t row0, int64_t k0, uint8_t *lds,
                                            int tid) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kPanelBytes / 16 / kThreads; ++i) {
     const int slot = tid + kThreads * i;
     const int r = slot >> 2, c = (slot & 3) ^ swz(r);
     const int64_t gr = min(row0 + r, d - 1);
@@ -137,22 +138,22 @@ __global__ void __launch_bounds__(kThreads)
 
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;  // sub-tile rows wm*128.., cols wn*64..
-  // On a diagonal tile the two lower-left sub-tiles lie below the diagonal;
-  // those two waves accumulate the float64 activation energy of the tile's
-  // rows (128 rows each) from the same LDS data instead.
-  const bool energy = diag && wm == 1 && wn < 2;
-  const int erow0 = wn * 128;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wm = wave >> 1, wn = wave & 1;  // sub-tile rows wm*128.., cols wn*128..
+  // On a diagonal tile the lower-left sub-tile lies below the diagonal; its
+  // wave accumulates the float64 activation energy of all 256 rows of the
+  // tile from the same LDS data instead.
+  const bool energy = diag && wm == 1 && wn == 0;
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  double en[2] = {0.0, 0.0};
+  double en[4] = {0.0, 0.0, 0.0, 0.0};
 
   auto issue = [&](int64_t ks) {
     uint8_t *base = smem + (ks % kStages) * kStageBytes;
@@ -161,106 +162,148 @@ __global__ void __launch_bounds__(kThreads)
   };
   auto energy_stage = [&](const uint8_t *A) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int r = erow0 + lane + 64 * q;
+    for (int q = 0; q < 4; ++q) {
+      const int r = lane + 64 * q;
+      u32x4_t v[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(A + r * kRowBytes + c * 16);
+      for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const u32x4_t *>(A + r * kRowBytes + c * 16);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const double lo = bf16_to_f64(v[e] & 0xffffu), hi = bf16_to_f64(v[e] >> 16);
+          const double lo = bf16_to_f64(v[c][e] & 0xffffu), hi = bf16_to_f64(v[c][e] >> 16);
           en[q] = fma(lo, lo, en[q]);
           en[q] = fma(hi, hi, en[q]);
         }
-      }
     }
   };
-  // One stage: fragments of both 16-token halves are read up front (the
-  // second half's reads overlap the first half's MFMAs); the stage's DMA for
-  // a later stage is issued between the reads and the MFMAs.
-  auto stage = [&](int buf, bool do_issue, int64_t next) {
-    const uint8_t *A = smem + buf * kStageBytes;
-    if (energy) {
-      if (do_issue) issue(next);
-      energy_stage(A);
-      return;
-    }
+  // Fragments of one 16-token half of a stage (4 of A, 4 of B).
+  auto read_half = [&](bf16x8_t (&fa)[4], bf16x8_t (&fb)[4], int64_t ks, int h) {
+    const uint8_t *A = smem + (ks % kStages) * kStageBytes;
     const uint8_t *B = diag ? A : A + kPanelBytes;
-    bf16x8_t a0[4], b0[2], a1[4], b1[2];
-    const int c0 = (lane >> 5), c1 = 2 + (lane >> 5);
+    const int c = 2 * h + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a0[i] = read_frag(A, wm * 128 + i * 32 + (lane & 31), c0);
+    for (int i = 0; i < 4; ++i) fa[i] = read_frag(A, wm * 128 + i * 32 + (lane & 31), c);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b0[j] = read_frag(B, wn * 64 + j * 32 + (lane & 31), c0);
-    if (do_issue) issue(next);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a1[i] = read_frag(A, wm * 128 + i * 32 + (lane & 31), c1);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) b1[j] = read_frag(B, wn * 64 + j * 32 + (lane & 31), c1);
+    for (int j = 0; j < 4; ++j) fb[j] = read_frag(B, wn * 128 + j * 32 + (lane & 31), c);
+  };
+  auto mfma_half = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  // copies per wave per stage
+  const int per_stage = diag ? kCopiesPerPanel : 2 * kCopiesPerPanel;
+  // wait until this wave's copies of stage `ks` have landed, with those of
+  // the later stages issued so far still in flight
+  auto wait_stage = [&](int64_t ks, int64_t issued_upto) {
+    const int outstanding = int(issued_upto - ks) * per_stage;
+    if (outstanding >= 24) vm_wait<24>();
+    else if (outstanding >= 16) vm_wait<16>();
+    else if (outstanding >= 12) vm_wait<12>();
+    else if (outstanding >= 8) vm_wait<8>();
+    else if (outstanding >= 4) vm_wait<4>();
+    else vm_wait<0>();
   };
 
+  // Pipeline: copies run up to three stages ahead of the stage being read.
+  // Iteration ks: the second half of stage ks is read while the first half's
+  // MFMAs run; then (all waves, barrier) stage ks+1 has landed and nobody
+  // reads stage ks's buffer any more, so stage ks+4 is issued into it, and
+  // the first half of stage ks+1 is read while the second half of stage ks
+  // is multiplied.  The energy wave runs the same barriers and copies and
+  // consumes stage ks before the barrier.  Every wave executes the same
+  // sequence of barriers.
   const int64_t nfull = n / kBK;
-  for (int64_t s = 0; s < nfull && s < kStages - 1; ++s) issue(s);
-  // per wave and stage: 2 copies per panel (1 panel on a diagonal tile)
-  for (int64_t ks = 0; ks < nfull; ++ks) {
-    // stage ks must have landed; stages ks+1, ks+2 may stay in flight
-    const int64_t ahead = min<int64_t>(2, nfull - 1 - ks);
-    if (diag) {
-      if (ahead == 2) vm_wait<4>();
-      else if (ahead == 1) vm_wait<2>();
-      else vm_wait<0>();
-    } else {
-      if (ahead == 2) vm_wait<8>();
-      else if (ahead == 1) vm_wait<4>();
-      else vm_wait<0>();
-    }
-    __builtin_amdgcn_s_barrier();  // all waves: stage ks landed, stage ks-1 consumed
-    stage(int(ks % kStages), ks + kStages - 1 < nfull, ks + kStages - 1);
-  }
-  if (nfull * kBK < n) {  // ragged token tail
+  auto prologue = [&]() {
+    const int64_t pro = min<int64_t>(nfull, kStages);
+    for (int64_t s = 0; s < pro; ++s) issue(s);
+    wait_stage(0, pro - 1);
+    __builtin_amdgcn_s_barrier();
+  };
+  auto sync_step = [&](int64_t ks) {
+    if (ks + 1 < nfull) wait_stage(ks + 1, min<int64_t>(nfull - 1, ks + 3));
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();
+    if (ks + kStages < nfull) issue(ks + kStages);
+  };
+  auto tail = [&]() {
     vm_wait<0>();
     __syncthreads();
     uint8_t *base = smem + (nfull % kStages) * kStageBytes;
     tail_panel(X, ld, d, n, I0, nfull * kBK, base, tid);
     if (!diag) tail_panel(X, ld, d, n, J0, nfull * kBK, base + kPanelBytes, tid);
     __syncthreads();
-    stage(int(nfull % kStages), false, 0);
+  };
+  if (energy) {
+    if (nfull > 0) prologue();
+    for (int64_t ks = 0; ks < nfull; ++ks) {
+      energy_stage(smem + (ks % kStages) * kStageBytes);
+      sync_step(ks);
+    }
+    if (nfull * kBK < n) {
+      tail();
+      energy_stage(smem + (nfull % kStages) * kStageBytes);
+    }
+  } else {
+    bf16x8_t xa[4], xb[4], ya[4], yb[4];
+    if (nfull > 0) {
+      prologue();
+      read_half(xa, xb, 0, 0);
+    }
+    for (int64_t ks = 0; ks < nfull; ++ks) {
+      read_half(ya, yb, ks, 1);
+      mfma_half(xa, xb);
+      sync_step(ks);
+      if (ks + 1 < nfull) read_half(xa, xb, ks + 1, 0);
+      mfma_half(ya, yb);
+    }
+    if (nfull * kBK < n) {
+      tail();
+      read_half(xa, xb, nfull, 0);
+      read_half(ya, yb, nfull, 1);
+      mfma_half(xa, xb);
+      mfma_half(ya, yb);
+    }
   }
 
   if (energy) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int64_t r = I0 + erow0 + lane + 64 * q;
+    for (int q = 0; q < 4; ++q) {
+      const int64_t r = I0 + lane + 64 * q;
       if (r < d) hdiag[r] += 2.0 * en[q];
     }
     return;
   }
   // Epilogue: H[i][j] += 2 * acc for i <= j inside the matrix.  32x32 MFMA
   // result layout: lane l, element v -> row 8*(v/4) + 4*(l/32) + v%4, col l%32.
+  // One 32-row band of the sub-tile (64 values per lane) at a time: all its
+  // loads are issued from clamped (valid) addresses before any store.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    float hv[4][16];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t gc = J0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 4; ++j) {
+      const int64_t gc = min(J0 + wn * 128 + j * 32 + (lane & 31), d - 1);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t gr =
+            min(I0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), d - 1);
+        hv[j][v] = H[gr * d + gc];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t gc = J0 + wn * 128 + j * 32 + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t gr = I0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (gr <= gc && gc < d) {
-          float *p = H + gr * d + gc;
-          *p = *p + 2.f * acc[i][j][v];
-        }
+        if (gr <= gc && gc < d) H[gr * d + gc] = hv[j][v] + 2.f * acc[i][j][v];
       }
     }
+  }
 }
 
 // fp32 inputs: plain LDS-tiled FMA SYRK on 64x64 upper tiles (fp32 products
