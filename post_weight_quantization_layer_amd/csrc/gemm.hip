@@ -128,6 +128,16 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmGroup g) {
     while ((tm + 1) * (tm + 2) / 2 <= tile) ++tm;
     while (tm * (tm + 1) / 2 > tile) --tm;
     tn = tile - tm * (tm + 1) / 2;
+  } else if (g.b_lower) {
+    // the K range shrinks as tn grows: columns left to right, heavy tiles first
+    const int tiles_m = (P.M + kTM - 1) / kTM;
+    tn = tile / tiles_m;
+    tm = tile % tiles_m;
+  } else if (g.a_lower) {
+    // the K range grows with tm: bottom row of tiles first
+    const int tiles_m = (P.M + kTM - 1) / kTM;
+    tm = tiles_m - 1 - tile / P.tiles_n;
+    tn = tile % P.tiles_n;
   } else {
     tm = tile / P.tiles_n;
     tn = tile % P.tiles_n;
