@@ -21,11 +21,12 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int kTile = 256;       // H tile edge
-constexpr int kBK = 32;          // tokens per pipeline stage
+constexpr int kBK = 64;          // tokens per pipeline stage
 constexpr int kThreads = 256;    // 4 waves (1 per SIMD), each a 128 x 128 sub-tile
-constexpr int kStages = 4;       // LDS ring depth
-constexpr int kRowBytes = kBK * 2;                 // 64 B of one X row per stage
-constexpr int kPanelBytes = kTile * kRowBytes;     // 16 KB per operand per stage
+constexpr int kStages = 2;       // LDS ring depth (double buffer)
+constexpr int kRowBytes = kBK * 2;                 // 128 B of one X row per stage
+constexpr int kChunks = kRowBytes / 16;            // 16-byte chunks per row
+constexpr int kPanelBytes = kTile * kRowBytes;     // 32 KB per operand per stage
 constexpr int kStageBytes = 2 * kPanelBytes;
 constexpr int kGroupRows = 4;    // tile-order band height (panel reuse in L2)
 
@@ -36,19 +37,21 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
 }
 
-// 16-byte chunk position inside a 64-byte LDS row, XOR-swizzled so that the
+// 16-byte chunk position inside a 128-byte LDS row, XOR-swizzled so that the
 // MFMA operand reads (lanes 0-31: rows 0-31 at chunk c, lanes 32-63: the
-// same rows at chunk c+1) spread over the LDS banks.  Measured on gfx950
-// with the LDS bank-conflict counter: this form is conflict-free for both
-// halves of a stage; (r>>1 ^ r>>3) and (r>>1) leave a 2-way conflict.
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// same rows at chunk c+1) spread over the LDS banks.  Picked with the LDS
+// bank-conflict counter on gfx950 among XOR and rotation candidates: this
+// one is conflict-free for all four 16-token steps of a stage.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-// Copy one 256-row x 32-token panel of X into LDS with global_load_lds
-// (16 bytes per lane; lane l of an instruction lands at base + 16 l), four
-// 1 KB blocks per wave.  Slot s of the panel is row s/4, swizzled position
-// s%4, so each lane fetches the global chunk that belongs at its slot (four
-// lanes cover one row's 64 contiguous bytes).  Rows past d are clamped to
-// row d-1 (they only feed outputs that are never stored).
+// Copy one 256-row x 64-token panel of X into LDS with global_load_lds
+// (16 bytes per lane; lane l of an instruction lands at base + 16 l), eight
+// 1 KB blocks per wave.  Slot s of the panel is row s/8, swizzled position
+// s%8, so each lane fetches the global chunk that belongs at its slot; eight
+// lanes cover one row's 128 contiguous bytes (a whole cache line, which
+// measured ~40% more copy throughput per CU than 64-byte row segments).
+// Rows past d are clamped to row d-1 (they only feed outputs that are never
+// stored).
 constexpr int kCopiesPerPanel = kPanelBytes / 1024 / (kThreads / 64);  // per wave
 __device__ __forceinline__ void issue_panel(const uint16_t *__restrict__ X, int64_t ld, int64_t d,
                                             int64_t row0, int64_t k0, uint8_t *lds, int wave,
@@ -57,7 +60,7 @@ __device__ __forceinline__ void issue_panel(const uint16_t *__restrict__ X, int6
   for (int i = 0; i < kCopiesPerPanel; ++i) {
     const int blk = wave * kCopiesPerPanel + i;
     const int slot = blk * 64 + lane;
-    const int r = slot >> 2, c = (slot & 3) ^ swz(r);
+    const int r = slot / kChunks, c = (slot % kChunks) ^ swz(r);
     const int64_t gr = min(row0 + r, d - 1);
     __builtin_amdgcn_global_load_lds((const void *)(X + gr * ld + k0 + c * 8),
                                      LDS_PTR(lds + blk * 1024), 16, 0, 0);
@@ -71,7 +74,7 @@ __device__ __forceinline__ void tail_panel(const uint16_t *__restrict__ X, int64
 #pragma unroll
   for (int i = 0; i < kPanelBytes / 16 / kThreads; ++i) {
     const int slot = tid + kThreads * i;
-    const int r = slot >> 2, c = (slot & 3) ^ swz(r);
+    const int r = slot / kChunks, c = (slot % kChunks) ^ swz(r);
     const int64_t gr = min(row0 + r, d - 1);
     const int64_t gk = k0 + c * 8;
     const uint16_t *p = X + gr * ld + gk;
@@ -122,7 +125,9 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) {
   return (double)__uint_as_float(bits16 << 16);
 }
 
-__global__ void __launch_bounds__(kThreads)
+// One workgroup per CU (128 KB of LDS) and one wave per SIMD: the kernel may
+// use the whole register file, so both fragment sets stay in registers.
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
     syrk_bf16_kernel(float *__restrict__ H, double *__restrict__ hdiag,
                      const uint16_t *__restrict__ X, int64_t d, int64_t n, int64_t ld, int nt,
                      int ntiles, int per_xcd) {
@@ -158,20 +163,28 @@ __global__ void __launch_bounds__(kThreads)
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   double en[4] = {0.0, 0.0, 0.0, 0.0};
 
+  // Copies of stage ks into its ring slot (one panel on a diagonal tile,
+  // whose B operand is its A panel).  Stages past the last full one re-load
+  // that one, so every iteration has the same shape; those extra copies
+  // land in a slot nobody reads before the tail path has waited for all
+  // copies.
+  const int64_t nfull = n / kBK;
   auto issue = [&](int64_t ks) {
     uint8_t *base = smem + (ks % kStages) * kStageBytes;
-    issue_panel(X, ld, d, I0, ks * kBK, base, wave, lane);
-    if (!diag) issue_panel(X, ld, d, J0, ks * kBK, base + kPanelBytes, wave, lane);
+    const int64_t k0 = min(ks, nfull - 1) * kBK;
+    issue_panel(X, ld, d, I0, k0, base, wave, lane);
+    if (!diag) issue_panel(X, ld, d, J0, k0, base + kPanelBytes, wave, lane);
   };
   auto energy_stage = [&](const uint8_t *A) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = lane + 64 * q;
-      u32x4_t v[4];
+      u32x4_t v[kChunks];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const u32x4_t *>(A + r * kRowBytes + c * 16);
+      for (int c = 0; c < kChunks; ++c)
+        v[c] = *reinterpret_cast<const u32x4_t *>(A + r * kRowBytes + c * 16);
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < kChunks; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const double lo = bf16_to_f64(v[c][e] & 0xffffu), hi = bf16_to_f64(v[c][e] >> 16);
@@ -180,8 +193,8 @@ __global__ void __launch_bounds__(kThreads)
         }
     }
   };
-  // Fragments of one 16-token half of a stage (4 of A, 4 of B).
-  auto read_half = [&](bf16x8_t (&fa)[4], bf16x8_t (&fb)[4], int64_t ks, int h) {
+  // Fragments of one 16-token step h (0..3) of a stage (4 of A, 4 of B).
+  auto read_step = [&](bf16x8_t (&fa)[4], bf16x8_t (&fb)[4], int64_t ks, int h) {
     const uint8_t *A = smem + (ks % kStages) * kStageBytes;
     const uint8_t *B = diag ? A : A + kPanelBytes;
     const int c = 2 * h + (lane >> 5);
@@ -190,48 +203,23 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
     for (int j = 0; j < 4; ++j) fb[j] = read_frag(B, wn * 128 + j * 32 + (lane & 31), c);
   };
-  auto mfma_half = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[4]) {
+  auto mfma_step = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
-  // copies per wave per stage
-  const int per_stage = diag ? kCopiesPerPanel : 2 * kCopiesPerPanel;
-  // wait until this wave's copies of stage `ks` have landed, with those of
-  // the later stages issued so far still in flight
-  auto wait_stage = [&](int64_t ks, int64_t issued_upto) {
-    const int outstanding = int(issued_upto - ks) * per_stage;
-    if (outstanding >= 24) vm_wait<24>();
-    else if (outstanding >= 16) vm_wait<16>();
-    else if (outstanding >= 12) vm_wait<12>();
-    else if (outstanding >= 8) vm_wait<8>();
-    else if (outstanding >= 4) vm_wait<4>();
-    else vm_wait<0>();
-  };
 
-  // Pipeline: copies run up to three stages ahead of the stage being read.
-  // Iteration ks: the second half of stage ks is read while the first half's
-  // MFMAs run; then (all waves, barrier) stage ks+1 has landed and nobody
-  // reads stage ks's buffer any more, so stage ks+4 is issued into it, and
-  // the first half of stage ks+1 is read while the second half of stage ks
-  // is multiplied.  The energy wave runs the same barriers and copies and
-  // consumes stage ks before the barrier.  Every wave executes the same
-  // sequence of barriers.
-  const int64_t nfull = n / kBK;
-  auto prologue = [&]() {
-    const int64_t pro = min<int64_t>(nfull, kStages);
-    for (int64_t s = 0; s < pro; ++s) issue(s);
-    wait_stage(0, pro - 1);
-    __builtin_amdgcn_s_barrier();
-  };
-  auto sync_step = [&](int64_t ks) {
-    if (ks + 1 < nfull) wait_stage(ks + 1, min<int64_t>(nfull - 1, ks + 3));
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
-    __builtin_amdgcn_s_barrier();
-    if (ks + kStages < nfull) issue(ks + kStages);
-  };
+  // Pipeline (double-buffered stages of 64 tokens, copies one stage ahead):
+  // the fragments of step h+1 are read while step h's MFMAs run (two
+  // register sets).  After step 2: this wave's copies of stage ks+1 have
+  // landed and (barrier) every wave's, and nobody reads stage ks's buffer
+  // any more, so stage ks+2 is issued into it and step 0 of stage ks+1 is
+  // read while step 3 of stage ks is multiplied.  The loop body has no
+  // branches; scheduling barriers keep each read group ahead of the MFMAs
+  // it overlaps.  The energy wave runs the same copies and barriers and
+  // consumes stage ks before the barrier.
   auto tail = [&]() {
     vm_wait<0>();
     __syncthreads();
@@ -240,11 +228,20 @@ __global__ void __launch_bounds__(kThreads)
     if (!diag) tail_panel(X, ld, d, n, J0, nfull * kBK, base + kPanelBytes, tid);
     __syncthreads();
   };
+  if (nfull > 0) {
+    issue(0);
+    issue(1);
+    if (diag) vm_wait<kCopiesPerPanel>();   // stage 0 landed, stage 1 in flight
+    else vm_wait<2 * kCopiesPerPanel>();
+    __builtin_amdgcn_s_barrier();
+  }
   if (energy) {
-    if (nfull > 0) prologue();
     for (int64_t ks = 0; ks < nfull; ++ks) {
       energy_stage(smem + (ks % kStages) * kStageBytes);
-      sync_step(ks);
+      vm_wait<0>();
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      issue(ks + kStages);
     }
     if (nfull * kBK < n) {
       tail();
@@ -252,23 +249,45 @@ __global__ void __launch_bounds__(kThreads)
     }
   } else {
     bf16x8_t xa[4], xb[4], ya[4], yb[4];
-    if (nfull > 0) {
-      prologue();
-      read_half(xa, xb, 0, 0);
-    }
+    if (nfull > 0) read_step(xa, xb, 0, 0);
     for (int64_t ks = 0; ks < nfull; ++ks) {
-      read_half(ya, yb, ks, 1);
-      mfma_half(xa, xb);
-      sync_step(ks);
-      if (ks + 1 < nfull) read_half(xa, xb, ks + 1, 0);
-      mfma_half(ya, yb);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): step 0's fragments are in
+      __builtin_amdgcn_sched_barrier(0);
+      read_step(ya, yb, ks, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(xa, xb);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_sched_barrier(0);
+      read_step(xa, xb, ks, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(ya, yb);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_sched_barrier(0);
+      read_step(ya, yb, ks, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(xa, xb);
+      __builtin_amdgcn_sched_barrier(0);
+      vm_wait<0>();
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage ks are done
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ks + kStages);
+      read_step(xa, xb, ks + 1, 0);  // past the last stage: unused
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(ya, yb);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (nfull * kBK < n) {
       tail();
-      read_half(xa, xb, nfull, 0);
-      read_half(ya, yb, nfull, 1);
-      mfma_half(xa, xb);
-      mfma_half(ya, yb);
+#pragma unroll
+      for (int h = 0; h < 4; h += 2) {
+        read_step(xa, xb, nfull, h);
+        read_step(ya, yb, nfull, h + 1);
+        mfma_step(xa, xb);
+        mfma_step(ya, yb);
+      }
     }
   }
 
