@@ -60,6 +60,18 @@ __device__ __forceinline__ void load_rows(const float *__restrict__ P, int64_t l
   }
 }
 
+// Interior form of load_rows: every row and k is in range, 16-byte aligned.
+template <int kT>
+__device__ __forceinline__ void load_rows_fast(const float *__restrict__ P, int64_t ld, int r0,
+                                               int k0, int tid, f32x4_t (&v)[Edge<kT>::kChunks]) {
+#pragma unroll
+  for (int i = 0; i < Edge<kT>::kChunks; ++i) {
+    const int c = tid + kThreads * i;
+    const int r = c / (kBK / 4), kc = (c % (kBK / 4)) * 4;
+    v[i] = *reinterpret_cast<const f32x4_t *>(P + int64_t(r0 + r) * ld + k0 + kc);
+  }
+}
+
 // Transposing store of a row-major staged tile into k-major LDS.
 template <int kT>
 __device__ __forceinline__ void store_rows_kmajor(float *lds, int tid,
@@ -95,6 +107,19 @@ __device__ __forceinline__ void load_kmajor(const float *__restrict__ P, int64_t
       }
     }
     v[i] = x;
+  }
+}
+
+// Interior form of load_kmajor.
+template <int kT>
+__device__ __forceinline__ void load_kmajor_fast(const float *__restrict__ P, int64_t ld, int c0,
+                                                 int k0, int tid, f32x4_t (&v)[Edge<kT>::kChunks]) {
+  constexpr int kPerRow = kT / 4;
+#pragma unroll
+  for (int i = 0; i < Edge<kT>::kChunks; ++i) {
+    const int c = tid + kThreads * i;
+    const int k = c / kPerRow, nc = (c % kPerRow) * 4;
+    v[i] = *reinterpret_cast<const f32x4_t *>(P + int64_t(k0 + k) * ld + c0 + nc);
   }
 }
 
@@ -183,8 +208,19 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmGroup g) {
 
   const int nsteps = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
   f32x4_t ra[Edge<kTM>::kChunks], rb[Edge<kTN>::kChunks];
+  // Interior tiles (the common case) take unconditional float4 loads; edge
+  // tiles and ragged k ranges take the masked loads.
+  const bool rows_in = m0 + kTM <= P.M && n0 + kTN <= P.N;
   auto load = [&](int s) {
     const int k0 = kbeg + s * kBK;
+    if (kVec && rows_in && k0 + kBK <= kend) {
+      load_rows_fast<kTM>(P.A, P.lda, m0, k0, tid, ra);
+      if (kTransB)
+        load_rows_fast<kTN>(P.B, P.ldb, n0, k0, tid, rb);
+      else
+        load_kmajor_fast<kTN>(P.B, P.ldb, n0, k0, tid, rb);
+      return;
+    }
     load_rows<kTM, kVec>(P.A, P.lda, P.M, m0, k0, kend, tid, ra);
     if (kTransB)
       load_rows<kTN, kVec>(P.B, P.ldb, P.N, n0, k0, kend, tid, rb);
@@ -208,19 +244,27 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmGroup g) {
       if (s + 1 < nsteps) load(s + 1);
       const float *A = As[buf];
       const float *B = Bs[buf];
+      // operands of step kk+1 are read while step kk's MFMAs run
+      float a[2][kFM], b[2][kFN];
+      auto rd = [&](int slot, int kk) {
+        const int k = kk * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < kFM; ++i) a[slot][i] = A[k * kPA + wm * kWM + i * 32 + (lane & 31)];
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) b[slot][j] = B[k * kPB + wn * kWN + j * 32 + (lane & 31)];
+      };
+      rd(0, 0);
 #pragma unroll
       for (int kk = 0; kk < kBK / 2; ++kk) {
-        const int k = kk * 2 + (lane >> 5);
-        float a[kFM], b[kFN];
-#pragma unroll
-        for (int i = 0; i < kFM; ++i) a[i] = A[k * kPA + wm * kWM + i * 32 + (lane & 31)];
-#pragma unroll
-        for (int j = 0; j < kFN; ++j) b[j] = B[k * kPB + wn * kWN + j * 32 + (lane & 31)];
+        if (kk + 1 < kBK / 2) rd((kk + 1) & 1, kk + 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < kFM; ++i)
 #pragma unroll
           for (int j = 0; j < kFN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[kk & 1][i], b[kk & 1][j], acc[i][j],
+                                                            0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (s + 1 < nsteps) store(buf ^ 1);
       __syncthreads();
