@@ -7,9 +7,11 @@
 // one read-modify-write per tile and the result is deterministic (no split-K
 // atomics).  X is d x n row-major (tokens contiguous), so both MFMA operands
 // are K-contiguous rows of X and no transpose is needed anywhere.  X panels
-// stream into a 4-deep LDS ring with direct global->LDS copies; on diagonal
-// tiles the wave whose sub-tile lies below the diagonal accumulates the
-// float64 activation energy of the tile's rows from the same LDS data.
+// stream through registers into a double-buffered LDS ring; on diagonal
+// tiles the four waves also accumulate the float64 activation energy of the
+// tile's rows from the same LDS data, in the shadow of their MFMAs.
+#include <type_traits>
+
 #include "common.h"
 
 namespace gptq {
@@ -44,28 +46,14 @@ __device__ __forceinline__ void vm_wait() {
 // one is conflict-free for all four 16-token steps of a stage.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-// Copy one 256-row x 64-token panel of X into LDS with global_load_lds
-// (16 bytes per lane; lane l of an instruction lands at base + 16 l), eight
-// 1 KB blocks per wave.  Slot s of the panel is row s/8, swizzled position
-// s%8, so each lane fetches the global chunk that belongs at its slot; eight
-// lanes cover one row's 128 contiguous bytes (a whole cache line, which
-// measured ~40% more copy throughput per CU than 64-byte row segments).
-// Rows past d are clamped to row d-1 (they only feed outputs that are never
-// stored).
-constexpr int kCopiesPerPanel = kPanelBytes / 1024 / (kThreads / 64);  // per wave
-__device__ __forceinline__ void issue_panel(const uint16_t *__restrict__ X, int64_t ld, int64_t d,
-                                            int64_t row0, int64_t k0, uint8_t *lds, int wave,
-                                            int lane) {
-#pragma unroll
-  for (int i = 0; i < kCopiesPerPanel; ++i) {
-    const int blk = wave * kCopiesPerPanel + i;
-    const int slot = blk * 64 + lane;
-    const int r = slot / kChunks, c = (slot % kChunks) ^ swz(r);
-    const int64_t gr = min(row0 + r, d - 1);
-    __builtin_amdgcn_global_load_lds((const void *)(X + gr * ld + k0 + c * 8),
-                                     LDS_PTR(lds + blk * 1024), 16, 0, 0);
-  }
-}
+// A stage (two 256-row x 64-token panels) reaches LDS through registers:
+// 16 loads of 16 bytes per lane.  On gfx950 ordinary loads sustained a
+// higher per-CU copy rate than direct global->LDS copies (about 56 GB/s per
+// CU with every CU streaming), and that rate, not the matrix cores, bounds
+// this kernel.  Rows past d are clamped to row d-1 (they only feed outputs
+// that are never stored).
+constexpr int kLoads = kStageBytes / 16 / kThreads;   // 16 per lane per stage
+constexpr int kPanelLoads = kLoads / 2;
 
 // Ragged last stage: register path with element masks (tokens >= n are 0).
 __device__ __forceinline__ void tail_panel(const uint16_t *__restrict__ X, int64_t ld, int64_t d,
@@ -149,11 +137,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;  // sub-tile rows wm*128.., cols wn*128..
-  // On a diagonal tile the lower-left sub-tile lies below the diagonal; its
-  // wave accumulates the float64 activation energy of all 256 rows of the
-  // tile from the same LDS data instead.
-  const bool energy = diag && wm == 1 && wn == 0;
-
   f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -161,144 +144,176 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  double en[4] = {0.0, 0.0, 0.0, 0.0};
+  // On a diagonal tile every wave also accumulates, in float64, the
+  // activation energy of one 64-row quarter of the tile's rows (row
+  // I0 + 64 wave + lane per lane) from the same LDS data, spread over its
+  // MFMA slots; the lower-left sub-tile is multiplied but never stored.
+  double en = 0.0;
+  const int erow = 64 * wave + lane;
 
-  // Copies of stage ks into its ring slot (one panel on a diagonal tile,
-  // whose B operand is its A panel).  Stages past the last full one re-load
-  // that one, so every iteration has the same shape; those extra copies
-  // land in a slot nobody reads before the tail path has waited for all
-  // copies.
+  // Stage ks is fetched into stg[] with ordinary 16-byte loads and stored to
+  // its LDS slot one iteration later.  Load q of a lane is row
+  // (tid/8 + 32 (q%8)) of panel q/8 (A: rows I0.., B: rows J0..; on a
+  // diagonal tile both are the same rows, which keeps every tile on one
+  // branch-free code path) at 16-byte chunk tid%8: eight lanes read one
+  // row's 128 contiguous bytes (a whole cache line).  Stages past the last
+  // full one re-load that one; that extra copy lands in a slot the tail
+  // path overwrites.
   const int64_t nfull = n / kBK;
-  auto issue = [&](int64_t ks) {
-    uint8_t *base = smem + (ks % kStages) * kStageBytes;
-    const int64_t k0 = min(ks, nfull - 1) * kBK;
-    issue_panel(X, ld, d, I0, k0, base, wave, lane);
-    if (!diag) issue_panel(X, ld, d, J0, k0, base + kPanelBytes, wave, lane);
+  const int lrow = tid >> 3, lchunk = tid & 7;
+  const int lds_off = lrow * kRowBytes + ((lchunk ^ swz(lrow)) << 4);
+  const uint16_t *rp[kLoads];
+#pragma unroll
+  for (int q = 0; q < kLoads; ++q)
+    rp[q] = X + min((q < kPanelLoads ? I0 : J0) + lrow + 32 * (q % kPanelLoads), d - 1) * ld +
+            lchunk * 8;
+  u32x4_t stg[kLoads];
+  auto load_one = [&](int q, int64_t ks) {
+    stg[q] = *reinterpret_cast<const u32x4_t *>(rp[q] + min(ks, nfull - 1) * kBK);
   };
-  auto energy_stage = [&](const uint8_t *A) {
+  auto store_one = [&](int q, int64_t ks) {
+    *reinterpret_cast<u32x4_t *>(smem + (ks % kStages) * kStageBytes + lds_off +
+                                 (q / kPanelLoads) * kPanelBytes +
+                                 (q % kPanelLoads) * 32 * kRowBytes) = stg[q];
+  };
+  // Energy inputs: the two 16-byte chunks (16 tokens) of this lane's row
+  // that 16-token step h of stage ks covers.
+  auto energy_read = [&](u32x4_t (&e)[2], int64_t ks, int h) {
+    const uint8_t *A = smem + (ks % kStages) * kStageBytes + erow * kRowBytes;
+    e[0] = *reinterpret_cast<const u32x4_t *>(A + (((2 * h) ^ swz(erow)) << 4));
+    e[1] = *reinterpret_cast<const u32x4_t *>(A + (((2 * h + 1) ^ swz(erow)) << 4));
+  };
+  // Token q of those 16, in token order.
+  auto energy_acc = [&](const u32x4_t (&e)[2], int q) {
+    const uint32_t w = e[q >> 3][(q >> 1) & 3];
+    const double v = bf16_to_f64((q & 1) ? (w >> 16) : (w & 0xffffu));
+    en = fma(v, v, en);
+  };
+  auto energy_stage = [&](int64_t ks) {
+    u32x4_t e[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = lane + 64 * q;
-      u32x4_t v[kChunks];
+    for (int h = 0; h < 4; ++h) {
+      energy_read(e, ks, h);
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c)
-        v[c] = *reinterpret_cast<const u32x4_t *>(A + r * kRowBytes + c * 16);
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const double lo = bf16_to_f64(v[c][e] & 0xffffu), hi = bf16_to_f64(v[c][e] >> 16);
-          en[q] = fma(lo, lo, en[q]);
-          en[q] = fma(hi, hi, en[q]);
-        }
+      for (int q = 0; q < 16; ++q) energy_acc(e, q);
     }
   };
-  // Fragments of one 16-token step h (0..3) of a stage (4 of A, 4 of B).
-  auto read_step = [&](bf16x8_t (&fa)[4], bf16x8_t (&fb)[4], int64_t ks, int h) {
+  // Fragment f of 16-token step h of stage ks, in the order the MFMAs of a
+  // step consume them: a0 b0 b1 b2 b3 a1 a2 a3.
+  auto read_one = [&](bf16x8_t (&fa)[4], bf16x8_t (&fb)[4], int64_t ks, int h, int f) {
     const uint8_t *A = smem + (ks % kStages) * kStageBytes;
-    const uint8_t *B = diag ? A : A + kPanelBytes;
     const int c = 2 * h + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = read_frag(A, wm * 128 + i * 32 + (lane & 31), c);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = read_frag(B, wn * 128 + j * 32 + (lane & 31), c);
+    if (f == 0) fa[0] = read_frag(A, wm * 128 + (lane & 31), c);
+    else if (f < 5) fb[f - 1] = read_frag(A + kPanelBytes, wn * 128 + (f - 1) * 32 + (lane & 31), c);
+    else fa[f - 4] = read_frag(A, wm * 128 + (f - 4) * 32 + (lane & 31), c);
   };
-  auto mfma_step = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[4]) {
+  auto read_step = [&](bf16x8_t (&fa)[4], bf16x8_t (&fb)[4], int64_t ks, int h) {
+#pragma unroll
+    for (int f = 0; f < 8; ++f) read_one(fa, fb, ks, h, f);
+  };
+  // The 16 MFMAs of one step; after MFMA q, hook(q) issues the memory
+  // operations planned for that slot, so that fragment reads, stage stores
+  // and global loads are spread over the matrix-core work instead of
+  // stalling it.
+  auto mfma_step = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[4], auto &&hook) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        hook(4 * i + j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
   };
 
-  // Pipeline (double-buffered stages of 64 tokens, copies one stage ahead):
-  // the fragments of step h+1 are read while step h's MFMAs run (two
-  // register sets).  After step 2: this wave's copies of stage ks+1 have
-  // landed and (barrier) every wave's, and nobody reads stage ks's buffer
-  // any more, so stage ks+2 is issued into it and step 0 of stage ks+1 is
-  // read while step 3 of stage ks is multiplied.  The loop body has no
-  // branches; scheduling barriers keep each read group ahead of the MFMAs
-  // it overlaps.  The energy wave runs the same copies and barriers and
-  // consumes stage ks before the barrier.
+  // Pipeline (double-buffered LDS stages of 64 tokens, one more stage in
+  // flight in registers).  Iteration ks multiplies stage ks in four 16-token
+  // steps; the fragments of step h+1 are read (one per two MFMAs) while the
+  // MFMAs of step h run.  During step 2 each slot also stores one register
+  // of stage ks+1 (loaded one iteration earlier) to the LDS slot that stage
+  // ks-1 used and re-issues that register's load for stage ks+2, so the
+  // copies stay in flight for a whole iteration.  A barrier then makes
+  // stage ks+1 visible (all reads of stage ks have completed by then), and
+  // step 0 of stage ks+1 is read while step 3 of stage ks is multiplied.
+  // On diagonal tiles each slot also adds one token of the lane's energy
+  // row, whose chunks are read one step ahead.
   auto tail = [&]() {
-    vm_wait<0>();
     __syncthreads();
     uint8_t *base = smem + (nfull % kStages) * kStageBytes;
     tail_panel(X, ld, d, n, I0, nfull * kBK, base, tid);
-    if (!diag) tail_panel(X, ld, d, n, J0, nfull * kBK, base + kPanelBytes, tid);
+    tail_panel(X, ld, d, n, J0, nfull * kBK, base + kPanelBytes, tid);
     __syncthreads();
   };
   if (nfull > 0) {
-    issue(0);
-    issue(1);
-    if (diag) vm_wait<kCopiesPerPanel>();   // stage 0 landed, stage 1 in flight
-    else vm_wait<2 * kCopiesPerPanel>();
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) load_one(q, 0);
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) store_one(q, 0);
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) load_one(q, 1);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
   }
-  if (energy) {
-    for (int64_t ks = 0; ks < nfull; ++ks) {
-      energy_stage(smem + (ks % kStages) * kStageBytes);
-      vm_wait<0>();
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-      __builtin_amdgcn_s_barrier();
-      issue(ks + kStages);
+  bf16x8_t xa[4], xb[4], ya[4], yb[4];
+  auto main_loop = [&](auto energy_tag) {
+    constexpr bool kEnergy = decltype(energy_tag)::value;
+    u32x4_t ep[2], eq[2];  // energy chunks of even / odd steps
+    if (nfull > 0) {
+      read_step(xa, xb, 0, 0);
+      if (kEnergy) energy_read(ep, 0, 0);
     }
-    if (nfull * kBK < n) {
-      tail();
-      energy_stage(smem + (nfull % kStages) * kStageBytes);
-    }
-  } else {
-    bf16x8_t xa[4], xb[4], ya[4], yb[4];
-    if (nfull > 0) read_step(xa, xb, 0, 0);
     for (int64_t ks = 0; ks < nfull; ++ks) {
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): step 0's fragments are in
-      __builtin_amdgcn_sched_barrier(0);
-      read_step(ya, yb, ks, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_step(xa, xb);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_sched_barrier(0);
-      read_step(xa, xb, ks, 2);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_step(ya, yb);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_sched_barrier(0);
-      read_step(ya, yb, ks, 3);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_step(xa, xb);
-      __builtin_amdgcn_sched_barrier(0);
-      vm_wait<0>();
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage ks are done
+      mfma_step(xa, xb, [&](int q) {
+        if (q & 1) read_one(ya, yb, ks, 1, q >> 1);
+        if (kEnergy) {
+          if (q == 0) energy_read(eq, ks, 1);
+          energy_acc(ep, q);
+        }
+      });
+      mfma_step(ya, yb, [&](int q) {
+        if (q & 1) read_one(xa, xb, ks, 2, q >> 1);
+        if (kEnergy) {
+          if (q == 0) energy_read(ep, ks, 2);
+          energy_acc(eq, q);
+        }
+      });
+      mfma_step(xa, xb, [&](int q) {
+        store_one(q, ks + 1);
+        load_one(q, ks + 2);
+        if (q & 1) read_one(ya, yb, ks, 3, q >> 1);
+        if (kEnergy) {
+          if (q == 0) energy_read(eq, ks, 3);
+          energy_acc(ep, q);
+        }
+      });
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): stores of ks+1, reads of ks done
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      issue(ks + kStages);
-      read_step(xa, xb, ks + 1, 0);  // past the last stage: unused
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_step(ya, yb);
-      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(ya, yb, [&](int q) {
+        if (q & 1) read_one(xa, xb, ks + 1, 0, q >> 1);  // past the last stage: unused
+        if (kEnergy) {
+          if (q == 0) energy_read(ep, ks + 1, 0);
+          energy_acc(eq, q);
+        }
+      });
     }
-    if (nfull * kBK < n) {
-      tail();
+  };
+  if (diag) main_loop(std::true_type{});
+  else main_loop(std::false_type{});
+  if (nfull * kBK < n) {
+    auto none = [](int) {};
+    tail();
 #pragma unroll
-      for (int h = 0; h < 4; h += 2) {
-        read_step(xa, xb, nfull, h);
-        read_step(ya, yb, nfull, h + 1);
-        mfma_step(xa, xb);
-        mfma_step(ya, yb);
-      }
+    for (int h = 0; h < 4; h += 2) {
+      read_step(xa, xb, nfull, h);
+      read_step(ya, yb, nfull, h + 1);
+      mfma_step(xa, xb, none);
+      mfma_step(ya, yb, none);
     }
+    if (diag) energy_stage(nfull);
   }
+  if (diag && I0 + erow < d) hdiag[I0 + erow] += 2.0 * en;
 
-  if (energy) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t r = I0 + lane + 64 * q;
-      if (r < d) hdiag[r] += 2.0 * en[q];
-    }
-    return;
-  }
   // Epilogue: H[i][j] += 2 * acc for i <= j inside the matrix.  32x32 MFMA
   // result layout: lane l, element v -> row 8*(v/4) + 4*(l/32) + v%4, col l%32.
   // One 32-row band of the sub-tile (64 values per lane) at a time: all its
