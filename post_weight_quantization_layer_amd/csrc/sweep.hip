@@ -20,6 +20,7 @@
 // and round-half-to-even (v_rndne_f32), fp16 super-scales with
 // round-to-nearest-even.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -132,61 +133,44 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Value of lane `sub` of this lane's 16-lane row, by a DPP row broadcast
+// (one VALU move; the source lane is an immediate).
+template <int kSub>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + kSub, 0xf, 0xf, false));
+}
+
+// rint(y) where y = num * (1/den) approximates num / den; *tie is set when y
+// lies within 1e-5 of a half-integer, where the exact quotient could round
+// the other way (see rint_div).
+__device__ __forceinline__ float rint_fast(float y, bool *tie) {
+  *tie |= fabsf(y - floorf(y) - 0.5f) < 1e-5f;
+  return __builtin_rintf(y);
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // kG8: the group size is a multiple of 8, so groups start only at the first
 // column of an 8-column step (the check runs once per 8 columns).
 template <int kQ4K, bool kG8>
 __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
-  // LDS: U's block (rows 0 .. Bp-1 of kMaxB floats, Bp = B rounded up to 8,
-  // rows and columns past B zero), then Bp reciprocals of the diagonal
-  // (zero past B, so padding steps change nothing).
-  extern __shared__ float Ub[];
+  // LDS: U's block (rows 0 .. Bp+1 of kMaxB floats, Bp = B rounded up to 8,
+  // rows and columns past B zero: the fast pass reads two rows ahead), then
+  // Bp + 2 reciprocals of the diagonal (zero past B, so padding steps change
+  // nothing).
+  extern __shared__ __align__(16) float Ub[];
   const int Bp = (a.B + 7) & ~7;
-  float *Uinv = Ub + (Bp + 1) * kMaxB;
+  float *Uinv = Ub + (Bp + 2) * kMaxB;
   const int tid = threadIdx.x;
   const int B = a.B;
   const int64_t ld = a.cols;
-  // U block: rows i1 .. i1+B-1, columns i1 .. i1+B-1.  Loads are issued in
-  // batches (all before any use) so their latencies overlap.
-  const float *Ublk = a.U + int64_t(a.i1) * ld + a.i1;
-  if ((ld & 3) == 0 && (a.i1 & 3) == 0 && (B & 3) == 0) {
-    const int nq = B * B / 4;  // float4 chunks (B/4 per row)
-    for (int e0 = tid; e0 < nq; e0 += kSweepThreads * 8) {
-      f32x4_t v[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int e = min(e0 + t * kSweepThreads, nq - 1);
-        const int j = e / (B / 4), k = (e % (B / 4)) * 4;
-        v[t] = *reinterpret_cast<const f32x4_t *>(Ublk + int64_t(j) * ld + k);
-      }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int e = e0 + t * kSweepThreads;
-        if (e < nq) {
-          const int j = e / (B / 4), k = (e % (B / 4)) * 4;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            Ub[j * kMaxB + k + x] = (k + x >= j) ? v[t][x] : 0.f;
-            if (k + x == j) Uinv[j] = 1.f / v[t][x];
-          }
-        }
-      }
-    }
-  } else {
-    for (int e = tid; e < B * B; e += kSweepThreads) {
-      const int j = e / B, k = e % B;
-      const float u = Ublk[int64_t(j) * ld + k];
-      Ub[j * kMaxB + k] = k >= j ? u : 0.f;
-      if (k == j) Uinv[j] = 1.f / u;
-    }
-  }
-  // columns past B of rows < B, and the padding rows B .. Bp (one extra row
-  // is read by the one-step-ahead prefetch), are zero
-  for (int e = tid; e < B * (kMaxB - B); e += kSweepThreads)
-    Ub[(e / (kMaxB - B)) * kMaxB + B + e % (kMaxB - B)] = 0.f;
-  for (int e = tid; e < (Bp + 1 - B) * kMaxB; e += kSweepThreads) Ub[B * kMaxB + e] = 0.f;
-  for (int j = B + tid; j < Bp + 1; j += kSweepThreads) Uinv[j] = 0.f;
-  __syncthreads();
-
   const int lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, sl = lane & 15;
   const int gbase = lane & 48;  // first lane of this row group
@@ -198,15 +182,15 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
   // 16-byte W accesses need a 4-float aligned row stride and block start
   const bool vec = (ld & 3) == 0 && (a.i1 & 3) == 0;
   const bool evec = (a.ldE & 3) == 0 && (reinterpret_cast<uintptr_t>(a.Err) & 15) == 0;
+  const bool full = vec && c0 + kCPL <= B;  // this lane's 8 columns, 16-byte accesses
 
-  for (int64_t r0 = (int64_t(blockIdx.x) * (kSweepThreads / 64) + wave) * 4; r0 < a.rows;
-       r0 += rows_per_pass) {
-    const int64_t row = r0 + grp;
-    const bool rv = row < a.rows;  // whole row group is valid or not
-    const int64_t rowc = rv ? row : a.rows - 1;
-    float *wrow = a.W + rowc * ld + a.i1;
-    float w[kCPL], q[kCPL], e[kCPL];
-    if (vec && c0 + kCPL <= B) {
+  // The first row group's weights are requested before the U block, so the
+  // two latencies overlap.
+  float w[kCPL];
+  auto load_w = [&](int64_t r0) {
+    const int64_t rowc = min(r0 + grp, a.rows - 1);
+    const float *wrow = a.W + rowc * ld + a.i1;
+    if (full) {
       const f32x4_t t0 = *reinterpret_cast<const f32x4_t *>(wrow + c0);
       const f32x4_t t1 = *reinterpret_cast<const f32x4_t *>(wrow + c0 + 4);
 #pragma unroll
@@ -218,8 +202,60 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
 #pragma unroll
       for (int x = 0; x < kCPL; ++x) w[x] = (c0 + x < B) ? wrow[c0 + x] : 0.f;
     }
+  };
+  int64_t r0 = (int64_t(blockIdx.x) * (kSweepThreads / 64) + wave) * 4;
+  if (r0 < a.rows) load_w(r0);
+
+  // U block: rows i1 .. i1+B-1, columns i1 .. i1+B-1, all loads of a thread
+  // in one batch before any use; the diagonal's reciprocals from loads of
+  // their own.
+  const float *Ublk = a.U + int64_t(a.i1) * ld + a.i1;
+  const float udiag = Ublk[int64_t(min(tid, B - 1)) * (ld + 1)];
+  if ((ld & 3) == 0 && (a.i1 & 3) == 0 && (B & 3) == 0) {
+    constexpr int kPer = kMaxB * kMaxB / 4 / kSweepThreads;  // float4 chunks per thread
+    const int nq = B * B / 4;
+    f32x4_t v[kPer];
 #pragma unroll
-    for (int x = 0; x < kCPL; ++x) q[x] = e[x] = 0.f;
+    for (int t = 0; t < kPer; ++t) {
+      const int e = min(tid + t * kSweepThreads, nq - 1);
+      const int j = e / (B / 4), k = (e % (B / 4)) * 4;
+      v[t] = *reinterpret_cast<const f32x4_t *>(Ublk + int64_t(j) * ld + k);
+    }
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      const int e = tid + t * kSweepThreads;
+      if (e < nq) {
+        const int j = e / (B / 4), k = (e % (B / 4)) * 4;
+        f32x4_t u;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) u[x] = (k + x >= j) ? v[t][x] : 0.f;
+        *reinterpret_cast<f32x4_t *>(Ub + j * kMaxB + k) = u;
+      }
+    }
+  } else {
+    for (int e = tid; e < B * B; e += kSweepThreads) {
+      const int j = e / B, k = e % B;
+      const float u = Ublk[int64_t(j) * ld + k];
+      Ub[j * kMaxB + k] = k >= j ? u : 0.f;
+    }
+  }
+  if (tid < B) Uinv[tid] = 1.f / udiag;
+  // columns past B of rows < B, and the padding rows B .. Bp+1, are zero
+  for (int e = tid; e < B * (kMaxB - B); e += kSweepThreads)
+    Ub[(e / (kMaxB - B)) * kMaxB + B + e % (kMaxB - B)] = 0.f;
+  for (int e = tid; e < (Bp + 2 - B) * kMaxB; e += kSweepThreads) Ub[B * kMaxB + e] = 0.f;
+  for (int j = B + tid; j < Bp + 2; j += kSweepThreads) Uinv[j] = 0.f;
+  __syncthreads();
+
+  for (; r0 < a.rows; r0 += rows_per_pass) {
+    // The row group's weights have arrived.  Waiting here explicitly keeps
+    // the compiler from waiting at every step instead, where the counter
+    // would also cover the previous steps' result stores.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    const int64_t row = r0 + grp;
+    const bool rv = row < a.rows;  // whole row group is valid or not
+    const int64_t rowc = rv ? row : a.rows - 1;
+    float *wrow = a.W + rowc * ld + a.i1;
 
     // grid state of the current group (per row group, identical in its lanes)
     float s = 1.f, rs = 1.f, z = 0.f;       // affine
@@ -339,74 +375,37 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
             rSv = Sv > 0.f ? 1.f / Sv : 0.f;
           }
     };
-    // U row j and 1/U_jj, fetched one step ahead
-    f32x4_t un0 = *reinterpret_cast<const f32x4_t *>(Ub + c0);
-    f32x4_t un1 = *reinterpret_cast<const f32x4_t *>(Ub + c0 + 4);
-    float uin = Uinv[0];
-    for (int j8 = 0; j8 < Bp; j8 += kCPL) {
-      if (kG8 && j8 == jg && j8 < B) {
-        jg += G;
-        choose_grid(j8);
+    // Q4_K: the grid values of the sub-block holding this lane's 8 columns
+    // (a 32-column sub-block spans 4 lanes), refreshed whenever a
+    // super-block's grid is chosen or read back.
+    float Sl = 0.f, Ml = 0.f, rSl = 0.f;
+    auto own_subblock = [&]() {
+      if (kQ4K) {
+        const int src = gbase + (((a.i1 & 255) + c0) >> 5);
+        Sl = shfl(Sv, src);
+        Ml = shfl(Mv, src);
+        rSl = shfl(rSv, src);
       }
-      const bool own = sl == (j8 >> 3);  // this lane owns columns j8 .. j8+7
-#pragma unroll
-      for (int x = 0; x < kCPL; ++x) {
-        const int j = j8 + x;
-        const int col = a.i1 + j;
-        const f32x4_t u0 = un0, u1 = un1;
-        const float uinv = uin;
-        un0 = *reinterpret_cast<const f32x4_t *>(Ub + (j + 1) * kMaxB + c0);
-        un1 = *reinterpret_cast<const f32x4_t *>(Ub + (j + 1) * kMaxB + c0 + 4);
-        uin = Uinv[j + 1];
-        if (!kG8 && j == jg && j < B) {
-          jg += G;
-          choose_grid(j);
-        }
-        const float wj = group_bcast(w[x], j >> 3, grp);
-        float qj, wq;
-        if (!kQ4K) {
-          qj = fminf(fmaxf(rint_div(wj, s, rs) + z, 0.f), maxq);
-          wq = s * (qj - z);
-        } else {
-          const int bsub = (col & 255) >> 5;
-          const float S = group_bcast(Sv, bsub, grp), M = group_bcast(Mv, bsub, grp);
-          qj = (S > 0.f) ? fminf(fmaxf(rint_div(wj + M, S, group_bcast(rSv, bsub, grp)), 0.f), 15.f)
-                         : 0.f;
-          wq = S * qj - M;
-        }
-        const float ej = (wj - wq) * uinv;
-        // No masks: U's block row j is zero left of the diagonal (and past B),
-        // and the owner's column j is overwritten with w^_j just below.
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          w[y] = fmaf(-ej, u0[y], w[y]);
-          w[4 + y] = fmaf(-ej, u1[y], w[4 + y]);
-        }
-        w[x] = own ? wq : w[x];
-        q[x] = own ? qj : q[x];
-        e[x] = own ? ej : e[x];
-      }
-    }
+    };
+    own_subblock();
 
-    if (rv) {
+    // Results of the current 8-column step (identical in all lanes of a row
+    // group: w^_j, code, e_j); its owner lane stores them after the step.
+    float wt[kCPL] = {}, qt[kCPL] = {}, et[kCPL] = {};
+    auto store_step = [&](int j8) {
+      if (!(rv && sl == (j8 >> 3))) return;
       uint8_t *qrow = a.q + row * ld + a.i1;
       float *erow = a.Err + row * a.ldE;
-      if (evec && c0 + kCPL <= B) {
-        *reinterpret_cast<f32x4_t *>(erow + c0) = f32x4_t{e[0], e[1], e[2], e[3]};
-        *reinterpret_cast<f32x4_t *>(erow + c0 + 4) = f32x4_t{e[4], e[5], e[6], e[7]};
-      } else {
-#pragma unroll
-        for (int x = 0; x < kCPL; ++x)
-          if (c0 + x < B) erow[c0 + x] = e[x];
-      }
-      if (vec && c0 + kCPL <= B) {
-        *reinterpret_cast<f32x4_t *>(wrow + c0) = f32x4_t{w[0], w[1], w[2], w[3]};
-        *reinterpret_cast<f32x4_t *>(wrow + c0 + 4) = f32x4_t{w[4], w[5], w[6], w[7]};
+      if (full && evec) {
+        *reinterpret_cast<f32x4_t *>(wrow + c0) = f32x4_t{wt[0], wt[1], wt[2], wt[3]};
+        *reinterpret_cast<f32x4_t *>(wrow + c0 + 4) = f32x4_t{wt[4], wt[5], wt[6], wt[7]};
+        *reinterpret_cast<f32x4_t *>(erow + c0) = f32x4_t{et[0], et[1], et[2], et[3]};
+        *reinterpret_cast<f32x4_t *>(erow + c0 + 4) = f32x4_t{et[4], et[5], et[6], et[7]};
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          lo |= uint32_t(q[x]) << (8 * x);
-          hi |= uint32_t(q[4 + x]) << (8 * x);
+          lo |= uint32_t(qt[x]) << (8 * x);
+          hi |= uint32_t(qt[4 + x]) << (8 * x);
         }
         *reinterpret_cast<uint32_t *>(qrow + c0) = lo;
         *reinterpret_cast<uint32_t *>(qrow + c0 + 4) = hi;
@@ -414,11 +413,154 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
 #pragma unroll
         for (int x = 0; x < kCPL; ++x)
           if (c0 + x < B) {
-            wrow[c0 + x] = w[x];
-            qrow[c0 + x] = (uint8_t)q[x];
+            wrow[c0 + x] = wt[x];
+            erow[c0 + x] = et[x];
+            qrow[c0 + x] = (uint8_t)qt[x];
           }
       }
+    };
+
+    // Column step j (block column) with the exact rounding and a generic
+    // broadcast: the path for group sizes that are not a multiple of 8, and
+    // the one a step is redone on when its fast pass saw a possible tie.
+    auto column_exact = [&](int j8, int x) {
+      const int j = j8 + x;
+      const int col = a.i1 + j;
+      const f32x4_t u0 = *reinterpret_cast<const f32x4_t *>(Ub + j * kMaxB + c0);
+      const f32x4_t u1 = *reinterpret_cast<const f32x4_t *>(Ub + j * kMaxB + c0 + 4);
+      const float uinv = Uinv[j];
+      if (!kG8 && j == jg && j < B) {
+        jg += G;
+        choose_grid(j);
+        own_subblock();
+      }
+      float wx = 0.f;  // w[x] without dynamic register indexing
+#pragma unroll
+      for (int y = 0; y < kCPL; ++y) wx = (y == x) ? w[y] : wx;
+      const float wj = group_bcast(wx, j >> 3, grp);
+      float qj, wq;
+      if (!kQ4K) {
+        qj = __builtin_amdgcn_fmed3f(rint_div(wj, s, rs) + z, 0.f, maxq);
+        wq = s * (qj - z);
+      } else {
+        const int bsub = (col & 255) >> 5;
+        const float S = group_bcast(Sv, bsub, grp), M = group_bcast(Mv, bsub, grp);
+        qj = (S > 0.f) ? __builtin_amdgcn_fmed3f(rint_div(wj + M, S, group_bcast(rSv, bsub, grp)),
+                                                 0.f, 15.f)
+                       : 0.f;
+        wq = S * qj - M;
+      }
+      const float ej = (wj - wq) * uinv;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        w[y] = fmaf(-ej, u0[y], w[y]);
+        w[4 + y] = fmaf(-ej, u1[y], w[4 + y]);
+      }
+#pragma unroll
+      for (int y = 0; y < kCPL; ++y) {
+        wt[y] = (y == x) ? wq : wt[y];
+        qt[y] = (y == x) ? qj : qt[y];
+        et[y] = (y == x) ? ej : et[y];
+      }
+    };
+
+    // U rows j and j+1 of the fast pass (read two columns ahead)
+    f32x4_t pa0 = *reinterpret_cast<const f32x4_t *>(Ub + c0);
+    f32x4_t pa1 = *reinterpret_cast<const f32x4_t *>(Ub + c0 + 4);
+    float pai = Uinv[0];
+    f32x4_t pb0 = *reinterpret_cast<const f32x4_t *>(Ub + kMaxB + c0);
+    f32x4_t pb1 = *reinterpret_cast<const f32x4_t *>(Ub + kMaxB + c0 + 4);
+    float pbi = Uinv[1];
+    // Fast pass over one 8-column step whose owner (lane j8/8 of each row)
+    // is the immediate kOwner, so that w_j is broadcast with one DPP move.
+    // It rounds w_j * (1/s) directly and tracks the largest distance of a
+    // rounded value from its integer: past 0.5 - 1e-5 the exact quotient
+    // could round the other way.
+    auto fast_step = [&](auto owner, float *tdist) {
+      constexpr int kOwner = decltype(owner)::value;
+      constexpr int j8 = kOwner * kCPL;
+      float S = 0.f, M = 0.f, rS = 0.f;
+      if (kQ4K) {  // the step's 8 columns lie in one sub-block
+        S = row_bcast<kOwner>(Sl);
+        M = row_bcast<kOwner>(Ml);
+        rS = row_bcast<kOwner>(rSl);
+      }
+      static_for<0, kCPL>([&](auto xs) {
+        constexpr int x = decltype(xs)::value;
+        constexpr int j = j8 + x;
+        const f32x4_t u0 = pa0, u1 = pa1;
+        const float uinv = pai;
+        pa0 = pb0;
+        pa1 = pb1;
+        pai = pbi;
+        pb0 = *reinterpret_cast<const f32x4_t *>(Ub + (j + 2) * kMaxB + c0);
+        pb1 = *reinterpret_cast<const f32x4_t *>(Ub + (j + 2) * kMaxB + c0 + 4);
+        pbi = Uinv[j + 2];
+        // keep these reads here: sunk next to their use they would stall
+        __builtin_amdgcn_sched_barrier(0);
+        const float wj = row_bcast<kOwner>(w[x]);
+        const float y = kQ4K ? (wj + M) * rS : wj * rs;
+        const float r = __builtin_rintf(y);
+        *tdist = fmaxf(*tdist, fabsf(y - r));
+        float qj, wq;
+        if (!kQ4K) {
+          qj = __builtin_amdgcn_fmed3f(r + z, 0.f, maxq);
+          wq = s * (qj - z);
+        } else {
+          qj = (S > 0.f) ? __builtin_amdgcn_fmed3f(r, 0.f, 15.f) : 0.f;
+          wq = S * qj - M;
+        }
+        const float ej = (wj - wq) * uinv;
+        // No masks: U's block row j is zero left of the diagonal (and past
+        // B); a lane's finished columns are never read again.
+#pragma unroll
+        for (int yy = 0; yy < 4; ++yy) {
+          w[yy] = fmaf(-ej, u0[yy], w[yy]);
+          w[4 + yy] = fmaf(-ej, u1[yy], w[4 + yy]);
+        }
+        wt[x] = wq;
+        qt[x] = qj;
+        et[x] = ej;
+      });
+    };
+
+    for (int j8 = 0; j8 < Bp; j8 += kCPL) {
+      if (!kG8) {  // a group may start at any column: exact path throughout
+#pragma unroll 1
+        for (int x = 0; x < kCPL; ++x) column_exact(j8, x);
+        store_step(j8);
+        continue;
+      }
+      if (j8 == jg && j8 < B) {
+        jg += G;
+        choose_grid(j8);
+        own_subblock();
+      }
+      float w0[kCPL];
+#pragma unroll
+      for (int yy = 0; yy < kCPL; ++yy) w0[yy] = w[yy];
+      float tdist = 0.f;
+      switch (j8 >> 3) {
+#define GPTQ_SWEEP_STEP(k) \
+  case k: fast_step(std::integral_constant<int, k>{}, &tdist); break;
+        GPTQ_SWEEP_STEP(0) GPTQ_SWEEP_STEP(1) GPTQ_SWEEP_STEP(2) GPTQ_SWEEP_STEP(3)
+        GPTQ_SWEEP_STEP(4) GPTQ_SWEEP_STEP(5) GPTQ_SWEEP_STEP(6) GPTQ_SWEEP_STEP(7)
+        GPTQ_SWEEP_STEP(8) GPTQ_SWEEP_STEP(9) GPTQ_SWEEP_STEP(10) GPTQ_SWEEP_STEP(11)
+        GPTQ_SWEEP_STEP(12) GPTQ_SWEEP_STEP(13) GPTQ_SWEEP_STEP(14) GPTQ_SWEEP_STEP(15)
+#undef GPTQ_SWEEP_STEP
+        default: break;
+      }
+      // a possible tie anywhere in the wave: redo the step from its saved
+      // state with the exact quotient (grids only change before a step)
+      if (__builtin_expect(__any(tdist > 0.5f - 1e-5f), 0)) {
+#pragma unroll
+        for (int yy = 0; yy < kCPL; ++yy) w[yy] = w0[yy];
+#pragma unroll 1
+        for (int x = 0; x < kCPL; ++x) column_exact(j8, x);
+      }
+      store_step(j8);
     }
+    if (r0 + rows_per_pass < a.rows) load_w(r0 + rows_per_pass);
   }
 }
 
@@ -555,19 +697,35 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   const int q4k = p.grid == GPTQ_GRID_Q4K;
   const int B = p.block;
   const size_t Bp = (B + 7) & ~7;
-  const size_t lds = ((Bp + 1) * kMaxB + Bp + 1) * sizeof(float);
+  const size_t lds = ((Bp + 2) * kMaxB + Bp + 2) * sizeof(float);
   const int g8 = (q4k ? 256 : p.group) % 8 == 0;
   const int variant = q4k * 2 + g8;
+  // (Q4_K groups are 256 columns, always a multiple of 8: variant 3)
   const void *kfn[4] = {(const void *)sweep_kernel<0, false>, (const void *)sweep_kernel<0, true>,
-                        (const void *)sweep_kernel<1, false>, (const void *)sweep_kernel<1, true>};
-  if (lds > 65536 && !g_sweep_lds_set[variant]) {
+                        (const void *)sweep_kernel<1, true>, (const void *)sweep_kernel<1, true>};
+  // A launch with no more workgroups than compute units gets one per CU (its
+  // LDS request is raised past half the CU's LDS), so that each wavefront
+  // has a SIMD to itself: the sweep is a chain of dependent steps per row,
+  // and a second wavefront on the SIMD would only halve its issue rate.
+  constexpr size_t kSoloLds = 96 * 1024;
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      n_cu = v;
+    else
+      n_cu = -1;
+  }
+  if (!g_sweep_lds_set[variant]) {
     hipError_t e = hipFuncSetAttribute(kfn[variant], hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+                                       (int)std::max(lds, kSoloLds));
     if (e != hipSuccess)
       return fail(GPTQ_ERR_DEVICE, std::string("cannot raise LDS limit: ") + hipGetErrorString(e));
     g_sweep_lds_set[variant] = true;
   }
   const unsigned nwg = (unsigned)std::min<int64_t>(cdiv(rows, kSweepThreads / 64 * 4), kSweepMaxWG);
+  const size_t lds_launch = (n_cu > 0 && nwg <= (unsigned)n_cu) ? std::max(lds, kSoloLds) : lds;
 
   SweepArgs a{};
   a.W = Wp;
@@ -610,10 +768,9 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
       a.B = Bc;
       a.Err = Err + (i1 - s1);
       switch (variant) {
-        case 0: GPTQ_TRY(launch(nm, sweep_kernel<0, false>, grid, blk, lds, stream, a)); break;
-        case 1: GPTQ_TRY(launch(nm, sweep_kernel<0, true>, grid, blk, lds, stream, a)); break;
-        case 2: GPTQ_TRY(launch(nm, sweep_kernel<1, false>, grid, blk, lds, stream, a)); break;
-        default: GPTQ_TRY(launch(nm, sweep_kernel<1, true>, grid, blk, lds, stream, a)); break;
+        case 0: GPTQ_TRY(launch(nm, sweep_kernel<0, false>, grid, blk, lds_launch, stream, a)); break;
+        case 1: GPTQ_TRY(launch(nm, sweep_kernel<0, true>, grid, blk, lds_launch, stream, a)); break;
+        default: GPTQ_TRY(launch(nm, sweep_kernel<1, true>, grid, blk, lds_launch, stream, a)); break;
       }
       const int64_t i2 = i1 + Bc;
       if (i2 < s2)
