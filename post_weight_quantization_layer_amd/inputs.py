@@ -34,6 +34,7 @@ import numpy as np
 
 TOKEN_CHUNK = 8192
 STREAM_W, STREAM_X, STREAM_OUTLIER, STREAM_X_GATE = 0, 1, 2, 3
+STREAM_STORED, STREAM_ACT16 = 4, 5
 BASE_SEED = 20261203
 
 
@@ -227,3 +228,50 @@ def x_chunk_storage(cfg: LayerConfig, tok0: int, ntok: int) -> np.ndarray:
 def token_chunks(cfg: LayerConfig, chunk_tokens: int):
     """(tok0, ntok) pairs that tile [0, tokens)."""
     return [(t, min(chunk_tokens, cfg.tokens - t)) for t in range(0, cfg.tokens, chunk_tokens)]
+
+
+# ------------------------------------------------- stored 4-bit layers (W4A16)
+@dataclass(frozen=True)
+class StoredLayer:
+    """A quantized layer as stored: codes, group index, scales, zero points."""
+
+    codes: np.ndarray   # (rows, cols) uint8 in [0, 16)
+    g_idx: np.ndarray   # (cols,) int32, group of each original column
+    scale: np.ndarray   # (rows, cols // group) float32 > 0
+    zero: np.ndarray    # (rows, cols // group) uint8 in [0, 16)
+    group: int
+
+
+def stored_int4_layer(rows: int, cols: int, group: int, act_order: bool, seed: int,
+                      w_sigma: float = 0.02) -> StoredLayer:
+    """Seeded stand-in for a 4-bit layer as it leaves quantization.
+
+    Codes and zero points are uniform over [0, 16).  Scales are spread around
+    the step of a min-max grid over a group of N(0, w_sigma^2) weights (about
+    0.35 w_sigma), log-normally.  With act_order the columns of each group are
+    a random subset of the row (a random processing order cut into groups of
+    ``group``); without it group g is columns [g*group, (g+1)*group)."""
+    assert cols % group == 0
+    ng = cols // group
+    g = _rng(seed, STREAM_STORED, 0, 0)
+    codes = g.integers(0, 16, size=(rows, cols), dtype=np.uint8)
+    zero = g.integers(0, 16, size=(rows, ng), dtype=np.uint8)
+    scale = (np.float32(0.35 * w_sigma)
+             * np.exp(np.float32(0.25) * g.standard_normal((rows, ng), dtype=np.float32)))
+    order = g.permutation(cols) if act_order else np.arange(cols)
+    g_idx = np.empty(cols, dtype=np.int32)
+    g_idx[order] = np.arange(cols, dtype=np.int32) // group
+    return StoredLayer(codes=codes, g_idx=g_idx, scale=scale.astype(np.float32),
+                       zero=zero, group=group)
+
+
+def activations_f16(batch: int, cols: int, seed: int, outlier_frac: float = 0.01,
+                    outlier_scale: float = 20.0) -> np.ndarray:
+    """(batch, cols) float16 bit patterns: N(0, 1) activations with a fraction
+    of channels scaled up, rounded to float16 (nearest, ties to even)."""
+    g = _rng(seed, STREAM_ACT16, 0, 0)
+    v = g.standard_normal((batch, cols), dtype=np.float32)
+    k = int(round(outlier_frac * cols))
+    if k:
+        v[:, g.choice(cols, size=k, replace=False)] *= np.float32(outlier_scale)
+    return v.astype(np.float16).view(np.uint16)
