@@ -10,6 +10,12 @@ Prints one JSON line.  The timed steps run without instrumentation; the
 per-kernel split and the roofline come from the same number of steps run
 again with the library's own HIP events recorded around every launch on the
 launch stream (gptq_profile_*).
+
+``--w4a16`` instead measures the W4A16 product of stored 4-bit layers
+(y = x W^T, int4 codes, fp16 activations) at several batch sizes, one JSON
+line per layer shape and batch.  Each call uses the next of several copies of
+the prepared layer, more than 1 GiB in all, so the weights come from HBM and
+not from the 256 MB last-level cache, as in a model whose layers run in turn.
 """
 from __future__ import annotations
 
@@ -117,6 +123,101 @@ def cpu_baseline(cfg, chunk_tokens):
                          "sweep": round(t_s * 1e3, 1), "pack": round(t_p * 1e3, 1)}}
 
 
+# W4A16 product workloads: the shapes of the quantization workloads, stored as
+# int4 with groups of 128 (rows, cols, group, activation order).
+W4A16_SHAPES = {
+    "q_proj_4096x4096_int4_g128": (4096, 4096, 128, False),
+    "down_proj_4096x11008_int4_g128_actorder": (4096, 11008, 128, True),
+    "up_proj_28672x8192_int4_g128_actorder": (28672, 8192, 128, True),
+    "mlp_14336x4096_int4_g128": (14336, 4096, 128, False),
+}
+W4A16_ROTATE_BYTES = 1 << 30
+
+
+def w4a16_bytes(rows, cols, group, batch):
+    """Algorithmic HBM bytes of one product: 4-bit codes, float32 scales,
+    4-bit zero points, fp16 x and y."""
+    ng = cols // group
+    return rows * cols // 2 + rows * ng * 4 + (rows * ng + 1) // 2 + 2 * batch * (cols + rows)
+
+
+def bench_w4a16(args):
+    import ctypes
+
+    import torch
+    from post_weight_quantization_layer_amd import binding as B
+    from post_weight_quantization_layer_amd.w4a16 import W4A16Linear
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    batches = [int(b) for b in args.w4a16_batches.split(",")]
+    shapes = args.w4a16_shapes.split(",") if args.w4a16_shapes else list(W4A16_SHAPES)
+    for name in shapes:
+        rows, cols, group, act = W4A16_SHAPES[name]
+        St = I.stored_int4_layer(rows, cols, group, act, seed=rows + cols)
+        base = W4A16Linear.from_codes(torch.from_numpy(St.codes).to(dev),
+                                      torch.from_numpy(St.g_idx).to(dev),
+                                      torch.from_numpy(St.scale).to(dev),
+                                      torch.from_numpy(St.zero).to(dev), group)
+        del St
+        copies = max(2, -(-W4A16_ROTATE_BYTES // base.mem.numel()))
+        mems = [base.mem] + [base.mem.clone() for _ in range(copies - 1)]
+        layers = []
+        for m in mems:
+            lay = B.gptq_w4a16_layer()
+            ctypes.pointer(lay)[0] = base.layer
+            lay.mem = m.data_ptr()
+            layers.append(lay)
+        torch.cuda.synchronize()
+        log(f"[w4a16] {name}: {copies} copies of {base.mem.numel() / 2**20:.1f} MiB")
+        for b in batches:
+            x = torch.from_numpy(I.activations_f16(b, cols, seed=b).view(np.int16)).to(dev)
+            x = x.view(torch.float16)
+            y = torch.empty((b, rows), dtype=torch.float16, device=dev)
+            nws = B.gptq_w4a16_workspace_bytes(layers[0], b)
+            ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+            iters = max(args.w4a16_iters, copies)
+            for i in range(copies):
+                B.gptq_w4a16_gemm(layers[i], x, y, ws)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(iters):
+                B.gptq_w4a16_gemm(layers[i % copies], x, y, ws)
+            e1.record()
+            e1.synchronize()
+            us_call = e0.elapsed_time(e1) * 1e3 / iters
+            B.gptq_profile_reset()
+            B.gptq_profile_enable(True)
+            for i in range(iters):
+                B.gptq_w4a16_gemm(layers[i % copies], x, y, ws)
+            torch.cuda.synchronize()
+            B.gptq_profile_enable(False)
+            n_g, ms_g = B.gptq_profile_query("w4a16_gemm")
+            n_x, ms_x = B.gptq_profile_query("w4a16_gather_x")
+            k_us = ms_g / n_g * 1e3
+            nbytes = w4a16_bytes(rows, cols, group, b)
+            gbs = nbytes / (k_us * 1e-6) / 1e9
+            line = {
+                "metric": "W4A16 product, HBM GB/s of the product kernel",
+                "value": round(gbs, 1), "unit": "GB/s", "higher_is_better": True,
+                "dtype": "int4 x f16 -> f32 sums -> f16", "data": "synthetic",
+                "config": {"workload": name, "rows": rows, "cols": cols, "group": group,
+                           "act_order": act, "batch": b},
+                "us_per_call": round(us_call, 2),
+                "kernel_us": {"w4a16_gemm": round(k_us, 2),
+                              "w4a16_gather_x": round(ms_x / n_x * 1e3, 2) if n_x else None},
+                "roofline": {"bound": "hbm", "kernel": "w4a16_gemm", "achieved": round(gbs, 1),
+                             "peak": PEAK["hbm"], "unit": "GB/s",
+                             "frac": round(gbs / PEAK["hbm"], 4), "traffic": None,
+                             "algorithmic_bytes_per_launch": nbytes},
+            }
+            print(json.dumps(line), flush=True)
+        del layers, mems, base
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,12 +230,20 @@ def main():
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run one plain streaming kernel of known size (read and write "
                          "1 GiB) before the steps, to scale rocprofv3 byte counters")
+    ap.add_argument("--w4a16", action="store_true",
+                    help="measure the W4A16 product of stored 4-bit layers instead")
+    ap.add_argument("--w4a16-batches", default="1,2,4,8,16,32,64")
+    ap.add_argument("--w4a16-shapes", default="")
+    ap.add_argument("--w4a16-iters", type=int, default=200)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(a layer's rows would shard across GPUs with one broadcast of U); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.w4a16:
+        bench_w4a16(args)
+        return
 
     import torch
     from post_weight_quantization_layer_amd import binding as B

@@ -190,6 +190,83 @@ gptq_status gptq_quantize_layer(float *W, int64_t rows, int64_t cols,
 gptq_status gptq_pack(const uint8_t *codes, int64_t rows, int64_t cols,
                       int32_t bits, uint32_t *packed, void *stream);
 
+/* ------------------------------------------------------------------ W4A16
+ * Running the stored layer: y = x W^T, with W^ rebuilt from 4-bit codes,
+ * per-group scale and zero inside the product kernel, activations in fp16
+ * ("Hugging Face AutoGPTQ and Transformers Integration", section Mixed
+ * Precision Scheme: int4 weights, fp16 activations, dequantization on the
+ * fly in a fused kernel; "GPTQ", section Waskie gardla: in inference the
+ * cost is reading memory).
+ *
+ * The stored layer is what gptq_quantize_layer (affine grid, bits = 4) and
+ * gptq_pack produce.  gptq_w4a16_prepare turns it once into the product
+ * kernel's layout; gptq_w4a16_gemm then runs any number of products.
+ */
+
+/* Host-side description of a prepared layer, filled by gptq_w4a16_prepare.
+ * The caller owns the struct and `mem`; treat the fields as read-only. */
+typedef struct {
+  int64_t rows;      /* out features                                         */
+  int64_t cols;      /* in features                                          */
+  int32_t group;     /* columns per group                                    */
+  int32_t permuted;  /* 1 when g_idx is not column / group (activation
+                        order): each product then first gathers x into
+                        group order in the workspace                        */
+  int64_t rows_pad;  /* rows rounded up to 16                                */
+  int64_t k_pad;     /* cols rounded up to 128                               */
+  void *mem;         /* device buffer given to gptq_w4a16_prepare            */
+  size_t mem_bytes;
+} gptq_w4a16_layer;
+
+/* Bytes of device memory a prepared layer needs (0 on invalid sizes). */
+size_t gptq_w4a16_layer_bytes(int64_t rows, int64_t cols, int32_t group);
+
+/*
+ * Prepare a 4-bit affine layer for gptq_w4a16_gemm.  SYNCHRONOUS: it waits
+ * for `stream`, because it validates g_idx on the device and reads the
+ * verdict back.
+ *
+ *  packed       rows x (cols/8) uint32: the codes as gptq_pack(bits = 4)
+ *               lays them out (original column order, LSB first).
+ *  g_idx        cols int32: group of each original column, in [0, cols/group);
+ *               every group must hold exactly `group` columns.
+ *  scale        rows x (cols/group) float, indexed by group.
+ *  zero_packed  the rows x (cols/group) zero points in [0, 16) as one 4-bit
+ *               LSB-first stream in row-major order (gptq_pack of the zero
+ *               matrix, as one row when a row alone is not 32-bit aligned);
+ *               ceil(rows*(cols/group)/8) uint32.
+ *  group        32, 64, or a multiple of 128; cols a multiple of group.
+ *  mem          device buffer, 256-byte aligned, >= gptq_w4a16_layer_bytes;
+ *               read-only for the products, which may run concurrently.
+ *  layer        out, host struct describing the prepared layer.
+ * The weight each product uses is w^[r][c] = scale[r][g] * (q[r][c] - z[r][g])
+ * with g = g_idx[c].  Returns GPTQ_ERR_INVALID_ARG when g_idx is out of range
+ * or a group's size differs from `group` (then `layer` is not filled).
+ */
+gptq_status gptq_w4a16_prepare(const uint32_t *packed, const int32_t *g_idx,
+                               const float *scale, const uint32_t *zero_packed,
+                               int64_t rows, int64_t cols, int32_t group,
+                               void *mem, size_t mem_bytes,
+                               gptq_w4a16_layer *layer, void *stream);
+
+/* Scratch bytes gptq_w4a16_gemm needs for `batch` rows of x. */
+size_t gptq_w4a16_workspace_bytes(const gptq_w4a16_layer *layer, int64_t batch);
+
+/*
+ * y = x W^T on the prepared layer.
+ *
+ *  x      batch x cols fp16 bit patterns, row-major, 16-byte aligned.
+ *  y      out, batch x rows fp16 (round to nearest even), row-major.
+ *  batch  1..4096.
+ *  ws     scratch, 256-byte aligned, >= gptq_w4a16_workspace_bytes.
+ * Products are formed exactly (fp16 activation times the integer q - z) and
+ * summed in float32; each group's sum is scaled by its float32 scale.  The
+ * summation order is fixed, so results are reproducible bit for bit.
+ */
+gptq_status gptq_w4a16_gemm(const gptq_w4a16_layer *layer, const uint16_t *x,
+                            int64_t batch, uint16_t *y, void *ws,
+                            size_t ws_bytes, void *stream);
+
 /*
  * Per-kernel timing with HIP events (for measurement, off by default).
  * When enabled, every kernel launch of the library is bracketed by a pair of

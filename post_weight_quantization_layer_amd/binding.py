@@ -22,6 +22,8 @@ EXPORTED = (
     "gptq_last_error", "gptq_workspace_bytes", "gptq_hessian_accumulate",
     "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_pack",
     "gptq_profile_enable", "gptq_profile_reset", "gptq_profile_query",
+    "gptq_w4a16_layer_bytes", "gptq_w4a16_prepare", "gptq_w4a16_workspace_bytes",
+    "gptq_w4a16_gemm",
 )
 
 
@@ -45,6 +47,13 @@ def make_params(bits: int, group: int, block: int, act_order: bool, percdamp: fl
                 grid: str | int = "affine") -> gptq_params:
     g = grid if isinstance(grid, int) else {"affine": GPTQ_GRID_AFFINE, "q4k": GPTQ_GRID_Q4K}[grid]
     return gptq_params(int(bits), int(group), int(block), int(bool(act_order)), float(percdamp), g)
+
+
+class gptq_w4a16_layer(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("group", ctypes.c_int32), ("permuted", ctypes.c_int32),
+                ("rows_pad", ctypes.c_int64), ("k_pad", ctypes.c_int64),
+                ("mem", ctypes.c_void_p), ("mem_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -80,6 +89,15 @@ def lib() -> ctypes.CDLL:
     L.gptq_profile_query.restype = I32
     L.gptq_profile_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(I64),
                                      ctypes.POINTER(ctypes.c_double)]
+    L.gptq_w4a16_layer_bytes.restype = SZ
+    L.gptq_w4a16_layer_bytes.argtypes = [I64, I64, I32]
+    L.gptq_w4a16_prepare.restype = I32
+    L.gptq_w4a16_prepare.argtypes = [P, P, P, P, I64, I64, I32, P, SZ,
+                                     ctypes.POINTER(gptq_w4a16_layer), P]
+    L.gptq_w4a16_workspace_bytes.restype = SZ
+    L.gptq_w4a16_workspace_bytes.argtypes = [ctypes.POINTER(gptq_w4a16_layer), I64]
+    L.gptq_w4a16_gemm.restype = I32
+    L.gptq_w4a16_gemm.argtypes = [ctypes.POINTER(gptq_w4a16_layer), P, I64, P, P, SZ, P]
     _lib = L
     return L
 
@@ -155,6 +173,37 @@ def gptq_pack(codes, bits: int, packed, rows: int | None = None, cols: int | Non
     r = codes.shape[0] if rows is None else rows
     c = codes.shape[1] if cols is None else cols
     _check(lib().gptq_pack(_ptr(codes), r, c, bits, _ptr(packed), _stream(stream)))
+
+
+def gptq_w4a16_layer_bytes(rows: int, cols: int, group: int) -> int:
+    n = lib().gptq_w4a16_layer_bytes(rows, cols, group)
+    if n == 0:
+        raise GptqError(GPTQ_ERR_INVALID_ARG, "invalid W4A16 layer shape or group")
+    return n
+
+
+def gptq_w4a16_prepare(packed, g_idx, scale, zero_packed, rows: int, cols: int, group: int,
+                       mem, stream=None) -> gptq_w4a16_layer:
+    """Synchronous.  ``mem`` must stay alive as long as the returned layer is used."""
+    layer = gptq_w4a16_layer()
+    _check(lib().gptq_w4a16_prepare(_ptr(packed), _ptr(g_idx), _ptr(scale), _ptr(zero_packed),
+                                    rows, cols, group, _ptr(mem),
+                                    mem.numel() * mem.element_size(), ctypes.byref(layer),
+                                    _stream(stream)))
+    return layer
+
+
+def gptq_w4a16_workspace_bytes(layer: gptq_w4a16_layer, batch: int) -> int:
+    return lib().gptq_w4a16_workspace_bytes(ctypes.byref(layer), batch)
+
+
+def gptq_w4a16_gemm(layer: gptq_w4a16_layer, x, y, ws=None, batch: int | None = None,
+                    stream=None):
+    """x (batch x cols) and y (batch x rows) float16 device tensors."""
+    b = x.shape[0] if batch is None else batch
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gptq_w4a16_gemm(ctypes.byref(layer), _ptr(x), b, _ptr(y), _ptr(ws), nbytes,
+                                 _stream(stream)))
 
 
 def gptq_profile_enable(on: bool = True):

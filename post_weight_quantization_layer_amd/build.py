@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgptq_mi355x.so")
-SOURCES = ["abi.hip", "hessian.hip", "gemm.hip", "prepare.hip", "sweep.hip", "pack.hip"]
+SOURCES = ["abi.hip", "hessian.hip", "gemm.hip", "prepare.hip", "sweep.hip", "pack.hip",
+           "w4a16.hip"]
 ARCH = "gfx950"
 
 

@@ -15,13 +15,13 @@ def declared_functions():
     with open(os.path.join(ROOT, "include", "gptq.h")) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gptq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gptq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     L = B.lib()
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.EXPORTED)
@@ -103,3 +103,62 @@ def test_pack_rejects_bad_args():
 
 def test_profile_query_unknown_kernel():
     assert B.gptq_profile_query("no_such_kernel") == (0, 0.0)
+
+
+# ------------------------------------------------------------------ W4A16
+def test_w4a16_layer_bytes():
+    n = B.gptq_w4a16_layer_bytes(4096, 11008, 128)
+    assert n >= 4096 * 11008 // 2 + 4096 * 86 * 4 + 11008 * 4
+    assert B.gptq_w4a16_layer_bytes(80, 96, 32) > 0   # ragged rows, padded columns
+    for bad in [(4096, 11008, 100), (4096, 11008, 96), (0, 128, 32), (16, 100, 32),
+                (16, 96, 64), (16, 384, 256)]:
+        with pytest.raises(B.GptqError):
+            B.gptq_w4a16_layer_bytes(*bad)
+
+
+def _prep(**kw):
+    a = dict(packed=FAKE, g_idx=FAKE, scale=FAKE, zero=FAKE, rows=64, cols=128, group=32,
+             mem=FAKE, mem_bytes=1 << 24)
+    a.update(kw)
+    layer = B.gptq_w4a16_layer()
+    st = B.lib().gptq_w4a16_prepare(a["packed"], a["g_idx"], a["scale"], a["zero"], a["rows"],
+                                    a["cols"], a["group"], a["mem"], a["mem_bytes"],
+                                    ctypes.byref(layer), None)
+    return st, B.gptq_last_error()
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(group=48), "group"),
+    (dict(cols=100), "group"),
+    (dict(rows=0), "rows"),
+    (dict(packed=None), "NULL"),
+    (dict(zero=None), "NULL"),
+    (dict(mem=ctypes.c_void_p(0x10010)), "aligned"),
+    (dict(mem_bytes=4096), "too small"),
+])
+def test_w4a16_prepare_rejects_before_any_launch(kw, msg):
+    st, err = _prep(**kw)
+    assert st == B.GPTQ_ERR_INVALID_ARG
+    assert msg in err
+
+
+def test_w4a16_gemm_rejects_before_any_launch():
+    L = B.lib()
+    empty = B.gptq_w4a16_layer()
+    assert L.gptq_w4a16_gemm(ctypes.byref(empty), FAKE, 1, FAKE, None, 0, None) == \
+        B.GPTQ_ERR_INVALID_ARG
+    assert "prepared" in B.gptq_last_error()
+    lay = B.gptq_w4a16_layer(rows=4096, cols=11008, group=128, permuted=1, rows_pad=4096,
+                             k_pad=11008, mem=0x10000, mem_bytes=1 << 30)
+    for batch in (0, 4097):
+        assert L.gptq_w4a16_gemm(ctypes.byref(lay), FAKE, batch, FAKE, None, 0, None) == \
+            B.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_w4a16_gemm(ctypes.byref(lay), ctypes.c_void_p(0x10008), 1, FAKE, None, 0,
+                             None) == B.GPTQ_ERR_INVALID_ARG
+    assert "aligned" in B.gptq_last_error()
+    need = B.gptq_w4a16_workspace_bytes(lay, 16)
+    assert need >= 16 * 11008 * 2           # the gathered activations
+    assert L.gptq_w4a16_gemm(ctypes.byref(lay), FAKE, 16, FAKE, None, 0, None) == \
+        B.GPTQ_ERR_WORKSPACE
+    assert L.gptq_w4a16_gemm(ctypes.byref(lay), FAKE, 16, FAKE, FAKE, need - 1, None) == \
+        B.GPTQ_ERR_WORKSPACE
