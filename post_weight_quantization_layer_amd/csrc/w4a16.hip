@@ -244,13 +244,27 @@ struct W4Args {
   int32_t splits, base, rem, ns_max;
 };
 
+// Masks and the fp16 1024.0 pair held in registers, so that each nibble
+// extraction is one v_and_or_b32 (two literal operands cannot be encoded).
+struct DqConst {
+  uint32_t lo, hi, magic;
+};
+
+__device__ inline DqConst dq_const() {
+  DqConst c;
+  asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(c.lo));
+  asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(c.hi));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(c.magic));
+  return c;
+}
+
 // B operand for one sub-step: the 8 codes of word w minus the zero point.
-__device__ inline h8_t dequant8(uint32_t w, uint32_t nz1, uint32_t nz2) {
+__device__ inline h8_t dequant8(uint32_t w, uint32_t nz1, uint32_t nz2, const DqConst &c) {
   const uint32_t w8 = w >> 8;
-  const uint32_t h0 = (w & 0x000F000Fu) | 0x64006400u;
-  const uint32_t h1 = (w & 0x00F000F0u) | 0x64006400u;
-  const uint32_t h2 = (w8 & 0x000F000Fu) | 0x64006400u;
-  const uint32_t h3 = (w8 & 0x00F000F0u) | 0x64006400u;
+  const uint32_t h0 = (w & c.lo) | c.magic;
+  const uint32_t h1 = (w & c.hi) | c.magic;
+  const uint32_t h2 = (w8 & c.lo) | c.magic;
+  const uint32_t h3 = (w8 & c.hi) | c.magic;
   const h2_t sixteenth = {_Float16(0.0625f), _Float16(0.0625f)};
   const h2_t z1 = __builtin_bit_cast(h2_t, nz1), z2 = __builtin_bit_cast(h2_t, nz2);
   const h2_t b01 = __builtin_bit_cast(h2_t, h0) + z1;
@@ -341,6 +355,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(W4Args a) {
     for (int j = 0; j < kNT; ++j) yacc[m][j] = f4_t{0.f, 0.f, 0.f, 0.f};
 
   const uint16_t *xa = xs + n * row_h + 8 * kg;  // lane's A row (m = n) and k offset
+  const DqConst dq = dq_const();
   // One step: 4 MFMA sub-steps per slab and tile; the scale of each unit is
   // applied to the unit's fp32 sum.
   auto step = [&](const int p) {
@@ -358,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(W4Args a) {
         const uint32_t z = (zb[p][j][u] >> (4 * (n & 7))) & 15u;
         const uint32_t nz1 = (0xE400u | z) * 0x00010001u;
         const uint32_t nz2 = (0xD400u | (z << 4)) * 0x00010001u;
-        const h8_t B = dequant8(wb[p][j][t], nz1, nz2);
+        const h8_t B = dequant8(wb[p][j][t], nz1, nz2, dq);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const f4_t c0 = (t % kSub == 0) ? f4_t{0.f, 0.f, 0.f, 0.f} : acc[m][j];
@@ -433,42 +448,53 @@ __global__ __launch_bounds__(kThreads) void w4a16_reduce_kernel(
   y[b * ldy + r] = __builtin_bit_cast(uint16_t, _Float16(sum));
 }
 
-// Small batches: one workgroup of W waves per 16 rows over all of K, so no
-// workgroup waits for another.  The `batch` rows of x (kernel order) are
-// staged in LDS once; wave w takes the steps w, w + W, w + 2W, ... with all of
-// its weights loaded up front, and the waves' 16 x 16 partial products are
-// summed through LDS in wave order.  NSW >= the steps of any wave (2, 4, 8).
+// Small batches: one workgroup of W waves per 16-row tile over all of K, so
+// no workgroup waits for another.  The `batch` rows of x (kernel order) are
+// staged in LDS; wave w takes the steps w, w + W, ... with all of its weights
+// loaded up front, and the waves' 16 x 16 partial products are summed through
+// LDS in wave order.  NSW >= the steps of any wave.  Layers with many row
+// tiles use small workgroups (4 waves), so that several workgroups per CU
+// have their loads in flight while others compute.
 template <int SPS, int NSW>
-__global__ __launch_bounds__(1024) void w4a16_rows_kernel(W4Args a) {
+struct RowTile {
+  u4_t w[NSW];
+  float s[NSW][SPS];
+  uint32_t z[NSW][SPS];
+};
+
+template <int SPS, int NSW>
+__global__ __launch_bounds__(NSW > 8 ? 512 : 1024) void w4a16_rows_kernel(W4Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int kSub = 4 / SPS;
   constexpr int kXChunks = 8;   // 16-byte x chunks staged per thread, at most
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthr = blockDim.x, W = nthr >> 6;
   const int n = lane & 15, kg = lane >> 4;
-  const int rt = blockIdx.x;
   const int row_h = a.ksteps * kStep + 8;   // LDS row stride in halves (+16 B)
   const int ns = (a.ksteps - wave + W - 1) / W;
   uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
+  float *red = reinterpret_cast<float *>(smem + size_t(a.batch) * row_h * 2);
 
-  u4_t wb[NSW];
-  float sb[NSW][SPS];
-  uint32_t zb[NSW][SPS];
-  auto issue = [&](int p) {
-    const int st = wave + min(p, ns - 1) * W;
-    wb[p] = a.wq[(int64_t(rt) * a.ksteps + st) * 64 + lane];
+  auto issue = [&](RowTile<SPS, NSW> &T, int rt) {
 #pragma unroll
-    for (int u = 0; u < SPS; ++u) {
-      const int64_t g = SPS == 1 ? st / a.gsteps : int64_t(st) * SPS + u;
-      sb[p][u] = a.sc[(int64_t(rt) * a.ngp + g) * 16 + n];
-      zb[p][u] = a.zp[(int64_t(rt) * a.ngp + g) * 2 + (n >> 3)];
+    for (int p = 0; p < NSW; ++p) {
+      const int st = wave + min(p, ns - 1) * W;
+      T.w[p] = a.wq[(int64_t(rt) * a.ksteps + st) * 64 + lane];
+#pragma unroll
+      for (int u = 0; u < SPS; ++u) {
+        const int64_t g = SPS == 1 ? st / a.gsteps : int64_t(st) * SPS + u;
+        T.s[p][u] = a.sc[(int64_t(rt) * a.ngp + g) * 16 + n];
+        T.z[p][u] = a.zp[(int64_t(rt) * a.ngp + g) * 2 + (n >> 3)];
+      }
     }
   };
 
-  // ---- x (issued first: loads complete in order), then every weight
+  RowTile<SPS, NSW> TA;
+  const int rt = blockIdx.x;
+
+  // ---- x (issued first: loads complete in order), then the first tile
   {
     const int cpr = a.ksteps * (kStep / 8);   // 16-byte chunks per row
-    const int total = a.batch * cpr;
     const int db = nthr / cpr, dc = nthr - db * cpr;
     int b0 = tid / cpr, c0 = tid - b0 * cpr;
     int bs[kXChunks], cs[kXChunks];
@@ -490,56 +516,56 @@ __global__ __launch_bounds__(1024) void w4a16_rows_kernel(W4Args a) {
       if (bs[i] < a.batch && cs[i] * 8 < a.cols)
         stg[i] = *reinterpret_cast<const u4_t *>(a.x + bs[i] * a.ldx + cs[i] * 8);
     }
-#pragma unroll
-    for (int p = 0; p < NSW; ++p) issue(p);
+    issue(TA, rt);
 #pragma unroll
     for (int i = 0; i < kXChunks; ++i)
       if (bs[i] < a.batch) *reinterpret_cast<u4_t *>(xs + bs[i] * row_h + cs[i] * 8) = stg[i];
-    (void)total;
   }
   __syncthreads();
 
-  f4_t yacc = {0.f, 0.f, 0.f, 0.f};
-  const bool has_row = n < a.batch;   // lane's A row m = n
-  const uint16_t *xa = xs + n * row_h + 8 * kg;
-  auto step = [&](const int p) {
-    const int st = wave + p * W;
-    f4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // Lane's A row m = n.  Rows m >= batch of C are never stored and depend only
+  // on row m of A, so those lanes read row batch - 1 instead of zeros.
+  const uint16_t *xa = xs + min(n, a.batch - 1) * row_h + 8 * kg;
+  const DqConst dq = dq_const();
+  auto tile = [&](const RowTile<SPS, NSW> &T, const int rtile) {
+    f4_t yacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      h8_t A = {};
-      if (has_row) A = *reinterpret_cast<const h8_t *>(xa + st * kStep + 32 * t);
-      const int u = t / kSub;
-      const uint32_t z = (zb[p][u] >> (4 * (n & 7))) & 15u;
-      const uint32_t nz1 = (0xE400u | z) * 0x00010001u;
-      const uint32_t nz2 = (0xD400u | (z << 4)) * 0x00010001u;
-      const h8_t B = dequant8(wb[p][t], nz1, nz2);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-          A, B, (t % kSub == 0) ? f4_t{0.f, 0.f, 0.f, 0.f} : acc, 0, 0, 0);
-      if (t % kSub == kSub - 1) {
-        const float sc = sb[p][u];
+    for (int p = 0; p < NSW; ++p) {
+      if (p >= ns) break;
+      const int st = wave + p * W;
+      f4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) yacc[i] = fmaf(sc, acc[i], yacc[i]);
+      for (int t = 0; t < 4; ++t) {
+        const h8_t A = *reinterpret_cast<const h8_t *>(xa + st * kStep + 32 * t);
+        const int u = t / kSub;
+        const uint32_t z = (T.z[p][u] >> (4 * (n & 7))) & 15u;
+        const uint32_t nz1 = (0xE400u | z) * 0x00010001u;
+        const uint32_t nz2 = (0xD400u | (z << 4)) * 0x00010001u;
+        const h8_t B = dequant8(T.w[p][t], nz1, nz2, dq);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            A, B, (t % kSub == 0) ? f4_t{0.f, 0.f, 0.f, 0.f} : acc, 0, 0, 0);
+        if (t % kSub == kSub - 1) {
+          const float sc = T.s[p][u];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) yacc[i] = fmaf(sc, acc[i], yacc[i]);
+        }
       }
     }
+    // sum the waves' partial products in wave order
+    *reinterpret_cast<f4_t *>(red + (wave * 64 + lane) * 4) = yacc;
+    __syncthreads();
+    for (int e = tid; e < 256; e += nthr) {   // 16 x 16 outputs; W may be below 4
+      const int l = e >> 2, i = e & 3;
+      float sum = 0.f;
+      for (int w = 0; w < W; ++w) sum += red[(w * 64 + l) * 4 + i];
+      const int b = 4 * (l >> 4) + i, r = rtile * 16 + (l & 15);
+      if (b < a.batch && r < a.rows)
+        a.y[b * a.ldy + r] = __builtin_bit_cast(uint16_t, _Float16(sum));
+    }
+    __syncthreads();
   };
-#pragma unroll
-  for (int p = 0; p < NSW; ++p)
-    if (p < ns) step(p);
 
-  // ---- sum the waves' partial products in wave order
-  __syncthreads();
-  float *red = reinterpret_cast<float *>(smem);
-  *reinterpret_cast<f4_t *>(red + (wave * 64 + lane) * 4) = yacc;
-  __syncthreads();
-  for (int e = tid; e < 256; e += nthr) {   // 16 x 16 outputs; W may be below 4
-    const int l = e >> 2, i = e & 3;
-    float sum = 0.f;
-    for (int w = 0; w < W; ++w) sum += red[(w * 64 + l) * 4 + i];
-    const int b = 4 * (l >> 4) + i, r = rt * 16 + (l & 15);
-    if (b < a.batch && r < a.rows)
-      a.y[b * a.ldy + r] = __builtin_bit_cast(uint16_t, _Float16(sum));
-  }
+  tile(TA, rt);
 }
 
 // ------------------------------------------------------------ launch plan
@@ -557,7 +583,7 @@ int cu_count() {
   return cached[dev];
 }
 
-constexpr size_t kRowsLdsMax = 128 * 1024;   // LDS of the rows kernel, at most
+constexpr size_t kRowsLdsMax = 144 * 1024;   // LDS of the rows kernel, at most
 constexpr int kRowsMaxBatch = 16;
 
 // Rows kernel (no split of K across workgroups): waves per workgroup and the
@@ -570,17 +596,22 @@ struct RowsPlan {
 RowsPlan rows_plan(const Geometry &g, int bc, int cus) {
   RowsPlan r{0, 0, 0};
   const size_t xbytes = size_t(bc) * (g.ksteps * kStep + 8) * 2;
-  if (bc > kRowsMaxBatch || xbytes > kRowsLdsMax) return r;
-  int w = g.rt16 >= 4 * cus ? 8 : 16;           // fewer row tiles: more waves per tile
-  while (w < 16 && int64_t(bc) * g.k_pad > int64_t(4096) * w) w *= 2;   // x staging capacity
-  if (int64_t(bc) * g.k_pad > int64_t(4096) * w) return r;
+  if (bc > kRowsMaxBatch || xbytes + 16 * 1024 > kRowsLdsMax) return r;
+  // steps a wave holds in registers: 16 (workgroups of at most 8 waves), 8
+  // (128 VGPRs), fewer with more scales per step
+  const int64_t max_ns = g.group == 32 ? 4 : g.group == 64 ? 8 : 16;
+  // many row tiles: small workgroups, several resident per CU; few: all 16
+  // waves of a CU on one tile
+  int w = g.rt16 >= 2 * cus ? 4 : 16;
+  while (w < 16 && (cdiv(g.ksteps, w) > max_ns || int64_t(bc) * g.k_pad > int64_t(4096) * w))
+    w *= 2;
   w = int(std::min<int64_t>(w, g.ksteps));
   const int64_t ns = cdiv(g.ksteps, w);
-  // groups of 32 (4 scales per step) keep at most 4 steps per wave in registers
-  if (ns > (g.group == 32 ? 4 : kMaxNs)) return r;
+  if (ns > max_ns || int64_t(bc) * g.k_pad > int64_t(4096) * w) return r;
+  if (ns > 8 && w > 8) return r;   // 16 steps per wave: at most 512 threads
   r.waves = w;
-  r.nsw = ns <= 2 ? 2 : ns <= 4 ? 4 : 8;
-  r.lds = std::max(xbytes, size_t(w) * 64 * 16);
+  r.nsw = ns <= 2 ? 2 : ns <= 4 ? 4 : ns <= 8 ? 8 : 16;
+  r.lds = xbytes + size_t(w) * 64 * 16;   // x, then the cross-wave sums
   return r;
 }
 
@@ -666,12 +697,15 @@ gptq_status launch_rows(const W4Args &a, const RowsPlan &r, hipStream_t stream) 
   return launch("w4a16_gemm", kern, dim3(a.rt16), dim3(64 * r.waves), r.lds, stream, a);
 }
 
+// Steps per wave: up to 16 with one scale per step, 8 with two, 4 with four.
 template <int SPS>
 gptq_status launch_rows_ns(const W4Args &a, const RowsPlan &r, hipStream_t stream) {
+  constexpr int k8 = SPS == 4 ? 4 : 8, k16 = SPS == 1 ? 16 : k8;
   switch (r.nsw) {
     case 2: return launch_rows<SPS, 2>(a, r, stream);
     case 4: return launch_rows<SPS, 4>(a, r, stream);
-    default: return launch_rows<SPS, SPS == 4 ? 4 : 8>(a, r, stream);   // SPS 4: nsw <= 4
+    case 8: return launch_rows<SPS, k8>(a, r, stream);
+    default: return launch_rows<SPS, k16>(a, r, stream);
   }
 }
 

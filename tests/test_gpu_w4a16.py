@@ -71,6 +71,8 @@ def check(y_bits, x_bits, L, rows=None, name=""):
     (37, 320, 64, True),     # columns padded to 384, groups of 64
     (21, 352, 32, True),     # columns padded to 384, groups of 32
     (64, 4096, 128, False),  # many split-K partials
+    (4200, 512, 128, True),  # more 16-row tiles than CUs: workgroups walk 1-2 tiles
+    (9600, 256, 64, False),  # 600 tiles: up to 3 per workgroup
 ])
 @pytest.mark.parametrize("batch", [1, 3, 16, 17, 40, 64, 70])
 def test_w4a16_matches_oracle(rows, cols, group, act, batch):
