@@ -21,6 +21,9 @@
  *   4. gptq_pack -- b-bit codes to a bit stream ("GPTQ", section
  *      Zlozonosc obliczeniowa: about 4.x bits per weight as stored).
  *
+ * The stored 4-bit layer then runs as y = x W^T through gptq_w4a16_prepare
+ * and gptq_w4a16_gemm (at the end of this header).
+ *
  * Conventions shared by every call:
  *  - Every pointer except `params` and the profiling outputs is a DEVICE
  *    pointer on the current HIP device, owned by the caller.  Buffers must

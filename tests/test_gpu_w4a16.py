@@ -74,7 +74,7 @@ def check(y_bits, x_bits, L, rows=None, name=""):
     (4200, 512, 128, True),  # more 16-row tiles than CUs: workgroups walk 1-2 tiles
     (9600, 256, 64, False),  # 600 tiles: up to 3 per workgroup
 ])
-@pytest.mark.parametrize("batch", [1, 3, 16, 17, 40, 64, 70])
+@pytest.mark.parametrize("batch", [1, 2, 3, 16, 17, 40, 64, 70])
 def test_w4a16_matches_oracle(rows, cols, group, act, batch):
     name = f"w4a16 {rows}x{cols} g{group} act={act} batch={batch}"
     log(name)
