@@ -178,40 +178,55 @@ def affine_quantize(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int):
     return q.astype(f32), (s * (q - z)).astype(f32)
 
 
-Q4K_SUB = 32      # weights per sub-block (6-bit scale and min each)
+Q4K_SUB = 32      # weights per sub-block (scale and min code each)
 Q4K_SUPER = 256   # weights per super-block (fp16 super-scale and super-min)
 
 
-def q4k_params(v: np.ndarray):
+def kquant_sub_bits(bits: int) -> int:
+    """Width of the sub-block scale and min codes of the two-level grid with
+    `bits`-bit weights.  "Add gguf q4_k quantization", review thread: 4-bit
+    sub-block scales and mins for the 2-bit type, 6-bit for the 3-, 4- and
+    5-bit types, 8-bit for the 6-bit type."""
+    widths = {2: 4, 3: 6, 4: 6, 5: 6, 6: 8}
+    if bits not in widths:
+        raise ValueError("the two-level grid has 2..6-bit codes")
+    return widths[bits]
+
+
+def q4k_params(v: np.ndarray, bits: int = 4):
     """Two-level grid of one super-block of 256 weights for each row.
 
     From "Add gguf q4_k quantization": w = q * block_scale + block_min with
-    6-bit sub-block scales and mins under a super-block scale, chosen by a
+    sub-block scale and min codes under a super-block scale, chosen by a
     plain min-max rule rather than gguf's search.  Reading used here (the
-    page gives the form, not the constants' derivation):
+    page gives the form, not the constants' derivation), with
+    maxq = 2^bits - 1 and kmax = 2^kquant_sub_bits(bits) - 1 (63 for the
+    4-bit codes of Q4_K):
 
     per sub-block b of 32: mn = min(v_b, 0), mx = max(v_b, 0),
-        s_b = (mx - mn)/15, m_b = -mn (>= 0);
-    D  = fp16(max_b s_b / 63), Dm = fp16(max_b m_b / 63);
-    sc_b = clamp(rint(s_b / D), 1, 63) if s_b > 0 and D > 0 else 0;
-    mc_b = clamp(rint(m_b / Dm), 0, 63) if Dm > 0 else 0;
+        s_b = (mx - mn)/maxq, m_b = -mn (>= 0);
+    D  = fp16(max_b s_b / kmax), Dm = fp16(max_b m_b / kmax);
+    sc_b = clamp(rint(s_b / D), 1, kmax) if s_b > 0 and D > 0 else 0;
+    mc_b = clamp(rint(m_b / Dm), 0, kmax) if Dm > 0 else 0;
     effective S_b = D sc_b, M_b = Dm mc_b.
 
     Returns D, Dm (float16), sc, mc (uint8, (rows, 8)), S, M (float32, (rows, 8))."""
+    maxq = f32(2 ** bits - 1)
+    kmax = f32(2 ** kquant_sub_bits(bits) - 1)
     v = np.asarray(v, dtype=f32)
     rows = v.shape[0]
     vb = v.reshape(rows, Q4K_SUPER // Q4K_SUB, Q4K_SUB)
     mn = np.minimum(vb.min(axis=2), f32(0))
     mx = np.maximum(vb.max(axis=2), f32(0))
-    s_b = (mx - mn) / f32(15)
+    s_b = (mx - mn) / maxq
     m_b = -mn
-    D = (s_b.max(axis=1) / f32(63)).astype(np.float16)
-    Dm = (m_b.max(axis=1) / f32(63)).astype(np.float16)
+    D = (s_b.max(axis=1) / kmax).astype(np.float16)
+    Dm = (m_b.max(axis=1) / kmax).astype(np.float16)
     Df = D.astype(f32)[:, None]
     Dmf = Dm.astype(f32)[:, None]
     with np.errstate(divide="ignore", invalid="ignore"):
-        sc = np.where((s_b > 0) & (Df > 0), np.clip(np.rint(s_b / Df), 1, 63), 0)
-        mc = np.where(Dmf > 0, np.clip(np.rint(m_b / Dmf), 0, 63), 0)
+        sc = np.where((s_b > 0) & (Df > 0), np.clip(np.rint(s_b / Df), 1, kmax), 0)
+        mc = np.where(Dmf > 0, np.clip(np.rint(m_b / Dmf), 0, kmax), 0)
     sc = sc.astype(f32)
     mc = mc.astype(f32)
     S = (Df * sc).astype(f32)
@@ -219,11 +234,12 @@ def q4k_params(v: np.ndarray):
     return D, Dm, sc.astype(np.uint8), mc.astype(np.uint8), S, M
 
 
-def q4k_quantize(w: np.ndarray, S: np.ndarray, M: np.ndarray):
-    """q = clamp(rint((w + M)/S), 0, 15) (0 when S = 0), w^ = S q - M."""
+def q4k_quantize(w: np.ndarray, S: np.ndarray, M: np.ndarray, bits: int = 4):
+    """q = clamp(rint((w + M)/S), 0, 2^bits - 1) (0 when S = 0), w^ = S q - M."""
     w = np.asarray(w, dtype=f32)
+    maxq = f32(2 ** bits - 1)
     with np.errstate(divide="ignore", invalid="ignore"):
-        q = np.where(S > 0, np.clip(np.rint((w + M) / S), 0, 15), 0).astype(f32)
+        q = np.where(S > 0, np.clip(np.rint((w + M) / S), 0, maxq), 0).astype(f32)
     return q, (S * q - M).astype(f32)
 
 
@@ -286,7 +302,7 @@ class _GroupState:
             s, z, zr = affine_params(v, sp.bits)
             self.scale[:, gi], self.zero[:, gi], self.zratio[:, gi] = s, z, zr
         else:
-            D, Dm, sc, mc, S, M = q4k_params(v)
+            D, Dm, sc, mc, S, M = q4k_params(v, sp.bits)
             b0 = j // Q4K_SUB
             nb = Q4K_SUPER // Q4K_SUB
             self.D[:, gi], self.Dm[:, gi] = D, Dm
@@ -295,7 +311,7 @@ class _GroupState:
             vb = np.asarray(v, f32).reshape(v.shape[0], nb, Q4K_SUB)
             mn = np.minimum(vb.min(axis=2), f32(0))
             mx = np.maximum(vb.max(axis=2), f32(0))
-            s_b = (mx - mn) / f32(15)
+            s_b = (mx - mn) / f32(2 ** sp.bits - 1)
             with np.errstate(divide="ignore", invalid="ignore"):
                 self.zratio[:, b0:b0 + nb] = s_b / D.astype(f32)[:, None]
                 self.mratio[:, b0:b0 + nb] = (-mn) / Dm.astype(f32)[:, None]
@@ -310,7 +326,7 @@ class _GroupState:
         else:
             b = j // Q4K_SUB
             S, M = self.scale[:, b], self.zero[:, b]
-            q, what = q4k_quantize(w, S, M)
+            q, what = q4k_quantize(w, S, M, sp.bits)
             with np.errstate(divide="ignore", invalid="ignore"):
                 ratio = (np.asarray(w, f32) + M) / S
         return q, what, ratio

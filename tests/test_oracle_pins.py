@@ -112,12 +112,12 @@ def _obs_bruteforce(Wp, Hp, spec):
             if spec.grid == "affine":
                 s, z, _ = O.affine_params(v, spec.bits)
             else:
-                _, _, _, _, S, M = O.q4k_params(v)
+                _, _, _, _, S, M = O.q4k_params(v, spec.bits)
         if spec.grid == "affine":
             q, wq = O.affine_quantize(W[:, j].astype(np.float32), s, z, spec.bits)
         else:
             b = (j % span) // O.Q4K_SUB
-            q, wq = O.q4k_quantize(W[:, j].astype(np.float32), S[:, b], M[:, b])
+            q, wq = O.q4k_quantize(W[:, j].astype(np.float32), S[:, b], M[:, b], spec.bits)
         R = np.arange(j + 1, d)
         if len(R):
             coef = np.linalg.solve(Hp[np.ix_(R, R)], Hp[R, j])
@@ -203,6 +203,8 @@ def test_diagonal_hessian_reduces_to_rtn():
     ("affine", 4, 16, [1, 8, 16, 32, 64, None]),
     ("affine", 3, 32, [1, 16, 32, 64, None]),
     ("q4k", 4, 256, [32, 64, 128, 256, 512, None]),
+    ("q4k", 2, 256, [64, 256, None]),
+    ("q4k", 6, 256, [128, None]),
 ])
 def test_blocked_equals_unblocked(grid, bits, group, blocks):
     rng = np.random.default_rng(7)
@@ -265,14 +267,18 @@ def test_affine_grid_membership(bits):
     np.testing.assert_array_equal(sw.what, (s * (sw.q - z)).astype(np.float32))
 
 
-def test_q4k_grid_membership():
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6])
+def test_q4k_grid_membership(bits):
     rng = np.random.default_rng(9)
     W, X = rand_layer(rng, 10, 512, 900)
-    res, _ = run(W, X, bits=4, group=256, block=128, act_order=False,
+    res, _ = run(W, X, bits=bits, group=256, block=128, act_order=False,
                  percdamp=0.01, grid="q4k")
     sw = res.sweep
-    assert sw.q.min() >= 0 and sw.q.max() <= 15
-    assert sw.sc.max() <= 63 and sw.mc.max() <= 63
+    kmax = 2 ** O.kquant_sub_bits(bits) - 1
+    assert sw.q.min() >= 0 and sw.q.max() <= 2 ** bits - 1
+    assert sw.q.max() == 2 ** bits - 1                 # the range is used
+    assert sw.sc.max() <= kmax and sw.mc.max() <= kmax
+    assert sw.sc.max() == kmax                         # the largest sub-scale sets D
     assert np.all(sw.sc >= 1)          # no all-zero sub-blocks here
     D = np.repeat(sw.D.astype(np.float32), 8, axis=1)
     Dm = np.repeat(sw.Dm.astype(np.float32), 8, axis=1)
@@ -422,3 +428,39 @@ def test_bits_per_weight_is_about_four_and_a_bit():
     b, g = 4, 128
     assert abs((b * g + 32 + b) / g - 4.28125) < 1e-12
     assert abs((4 * 256 + 8 * 12 + 32) / 256 - 4.5) < 1e-12
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6])
+def test_kquant_exact_grid_is_recovered(bits):
+    """A super-block built on a two-level grid -- fp16-exact D and Dm, integer
+    sub-scale and min codes with the largest at the code limit, and every
+    sub-block spanning codes 0..maxq -- is recovered exactly by the min-max
+    rule: same codes, zero error.  Sub-block code widths per the pages: 4
+    bits for the 2-bit type, 6 for 3..5, 8 for 6."""
+    assert O.kquant_sub_bits(bits) == {2: 4, 3: 6, 4: 6, 5: 6, 6: 8}[bits]
+    maxq = 2 ** bits - 1
+    kmax = 2 ** O.kquant_sub_bits(bits) - 1
+    rng = np.random.default_rng(40 + bits)
+    D, Dm = 2.0 ** -10, 2.0 ** -11
+    sc = rng.integers(1, kmax + 1, size=8)
+    sc[3] = sc[5] = kmax
+    mc = rng.integers(0, kmax + 1, size=8)
+    mc[5] = kmax                       # fits: S_5 maxq = D kmax maxq > Dm kmax
+    S, M = D * sc, Dm * mc
+    # keep max(v_b) = S_b maxq - M_b >= 0, so that the range [min(v,0), max(v,0)]
+    # is exactly [-M_b, S_b maxq - M_b]
+    mc = np.floor(np.minimum(M, S * maxq) / Dm).astype(np.int64)
+    M = Dm * mc
+    codes = rng.integers(0, maxq + 1, size=(8, 32))
+    codes[:, 0], codes[:, 1] = 0, maxq
+    v = (S[:, None] * codes - M[:, None]).reshape(1, 256).astype(np.float32)
+    Dh, Dmh, sc_o, mc_o, S_o, M_o = O.q4k_params(v, bits)
+    assert mc.max() == kmax
+    assert float(Dmh[0]) == Dm
+    np.testing.assert_array_equal(mc_o[0], mc)
+    assert float(Dh[0]) == D
+    np.testing.assert_array_equal(sc_o[0], sc)
+    for b in range(8):
+        q, wq = O.q4k_quantize(v[:, 32 * b:32 * b + 32], S_o[:, b:b + 1], M_o[:, b:b + 1], bits)
+        np.testing.assert_array_equal(q[0], codes[b])
+        np.testing.assert_array_equal(wq, v[:, 32 * b:32 * b + 32])
