@@ -64,14 +64,17 @@ typedef enum { GPTQ_DT_F32 = 0, GPTQ_DT_BF16 = 1 } gptq_dtype;
 
 typedef enum {
   GPTQ_GRID_AFFINE = 0, /* asymmetric min-max scale + integer zero per group  */
-  GPTQ_GRID_Q4K = 1     /* two-level: 6-bit sub-block scale/min (32 weights)
-                           under fp16 super-scale/super-min (256 weights)     */
+  GPTQ_GRID_Q4K = 1     /* two-level k-quant grid: sub-block scale/min codes
+                           (32 weights) under fp16 super-scale/super-min (256
+                           weights); Q4_K for bits = 4                        */
 } gptq_grid;
 
 /* Hyper-parameters ("GPTQ", section Hiperparametry: target precision, weights
  * per scale, activation order, value added to the Hessian diagonal). */
 typedef struct {
-  int32_t bits;      /* AFFINE: 2..8; Q4K: must be 4                           */
+  int32_t bits;      /* AFFINE: 2..8; Q4K: 2..6 (the sub-block scale/min codes
+                        are 4 bits wide for bits = 2, 6 for 3..5, 8 for 6:
+                        "Add gguf q4_k quantization", review thread)         */
   int32_t group;     /* AFFINE: weights per scale, divides cols (cols = one
                         group per row); Q4K: must be 256                      */
   int32_t block;     /* lazy-update block B, 1..128; group % B == 0 or
@@ -163,7 +166,9 @@ gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d,
  *           w^ = scale * (q - zero).
  *  Q4K (else pass NULL):
  *   q4k_super_scale, q4k_super_min  out, rows x (cols/256) fp16 bit patterns.
- *   q4k_sub_scale, q4k_sub_min      out, rows x (cols/32) bytes in [0, 63].
+ *   q4k_sub_scale, q4k_sub_min      out, rows x (cols/32) bytes in
+ *                                   [0, kmax], kmax = 15, 63 or 255 for
+ *                                   4-, 6- or 8-bit sub-block codes.
  *           w^ = (D * sc) * q - (Dm * mc).
  *  ws       scratch, >= gptq_workspace_bytes(rows, cols, p).
  */

@@ -107,8 +107,8 @@ static gptq_status check_params(const gptq_params *p, int64_t cols) {
     return fail(GPTQ_ERR_INVALID_ARG, "grid must be GPTQ_GRID_AFFINE or GPTQ_GRID_Q4K");
   if (p->grid == GPTQ_GRID_AFFINE && (p->bits < 2 || p->bits > 8))
     return fail(GPTQ_ERR_INVALID_ARG, "bits must be in [2, 8] for the affine grid");
-  if (p->grid == GPTQ_GRID_Q4K && p->bits != 4)
-    return fail(GPTQ_ERR_INVALID_ARG, "the Q4K grid has 4-bit codes (bits = 4)");
+  if (p->grid == GPTQ_GRID_Q4K && (p->bits < 2 || p->bits > 6))
+    return fail(GPTQ_ERR_INVALID_ARG, "bits must be in [2, 6] for the two-level (Q4K) grid");
   if (p->grid == GPTQ_GRID_Q4K && p->group != 256)
     return fail(GPTQ_ERR_INVALID_ARG, "the Q4K grid has 256-weight super-blocks (group = 256)");
   if (p->group < 1) return fail(GPTQ_ERR_INVALID_ARG, "group must be >= 1");

@@ -41,6 +41,7 @@ struct SweepArgs {
   int64_t rows, cols;
   int i1, B;
   int bits, group;
+  int sub_bits;    // two-level grid: width of the sub-block scale/min codes
   float *scale;    // affine: rows x (cols/group)
   uint8_t *zero;
   uint16_t *D, *Dm;   // q4k: rows x (cols/256)
@@ -177,6 +178,7 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
   const int c0 = sl * kCPL;     // first block column owned by this lane
   const int G = kQ4K ? 256 : a.group;
   const float maxq = float((1 << a.bits) - 1);
+  const float kmax = float((1 << a.sub_bits) - 1);   // two-level grid: sub-code limit
   const int64_t ngroups = a.cols / G;
   const int64_t rows_per_pass = int64_t(gridDim.x) * (kSweepThreads / 64) * 4;
   // 16-byte W accesses need a 4-float aligned row stride and block start
@@ -335,24 +337,24 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
               mx = fmaxf(mx, __shfl_xor(mx, 2));
               mn = fminf(mn, 0.f);
               mx = fmaxf(mx, 0.f);
-              sb_s[t] = (mx - mn) / 15.f;
+              sb_s[t] = (mx - mn) / maxq;
               sb_m[t] = -mn;
               smax = fmaxf(smax, sb_s[t]);
               mmax = fmaxf(mmax, sb_m[t]);
             }
             smax = group_max(smax);
             mmax = group_max(mmax);
-            const uint16_t Dh = f32_to_f16_rne(smax / 63.f);
-            const uint16_t Dmh = f32_to_f16_rne(mmax / 63.f);
+            const uint16_t Dh = f32_to_f16_rne(smax / kmax);
+            const uint16_t Dmh = f32_to_f16_rne(mmax / kmax);
             const float Df = f16_to_f32(Dh), Dmf = f16_to_f32(Dmh);
             float Sb[2], Mb[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
               const float scq = (sb_s[t] > 0.f && Df > 0.f)
-                                    ? fminf(fmaxf(__builtin_rintf(sb_s[t] / Df), 1.f), 63.f)
+                                    ? fminf(fmaxf(__builtin_rintf(sb_s[t] / Df), 1.f), kmax)
                                     : 0.f;
               const float mcq =
-                  (Dmf > 0.f) ? fminf(fmaxf(__builtin_rintf(sb_m[t] / Dmf), 0.f), 63.f) : 0.f;
+                  (Dmf > 0.f) ? fminf(fmaxf(__builtin_rintf(sb_m[t] / Dmf), 0.f), kmax) : 0.f;
               Sb[t] = Df * scq;
               Mb[t] = Dmf * mcq;
               if ((sl & 3) == 0 && rv) {
@@ -446,7 +448,7 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
         const int bsub = (col & 255) >> 5;
         const float S = group_bcast(Sv, bsub, grp), M = group_bcast(Mv, bsub, grp);
         qj = (S > 0.f) ? __builtin_amdgcn_fmed3f(rint_div(wj + M, S, group_bcast(rSv, bsub, grp)),
-                                                 0.f, 15.f)
+                                                 0.f, maxq)
                        : 0.f;
         wq = S * qj - M;
       }
@@ -507,7 +509,7 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
           qj = __builtin_amdgcn_fmed3f(r + z, 0.f, maxq);
           wq = s * (qj - z);
         } else {
-          qj = (S > 0.f) ? __builtin_amdgcn_fmed3f(r, 0.f, 15.f) : 0.f;
+          qj = (S > 0.f) ? __builtin_amdgcn_fmed3f(r, 0.f, maxq) : 0.f;
           wq = S * qj - M;
         }
         const float ej = (wj - wq) * uinv;
@@ -735,6 +737,7 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   a.cols = cols;
   a.bits = p.bits;
   a.group = p.group;
+  a.sub_bits = p.bits == 2 ? 4 : p.bits == 6 ? 8 : 6;
   a.scale = scale;
   a.zero = zero;
   a.D = D;

@@ -50,7 +50,8 @@ FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
     (dict(act_order=2), "act_order"),
     (dict(percdamp=-1.0), "percdamp"),
     (dict(percdamp=float("nan")), "percdamp"),
-    (dict(grid=1, bits=3, group=256), "4-bit"),
+    (dict(grid=1, bits=7, group=256), "[2, 6]"),
+    (dict(grid=1, bits=1, group=256), "[2, 6]"),
     (dict(grid=1, bits=4, group=128), "256"),
     (dict(grid=7), "grid"),
     (dict(group=96, block=32), "multiple of group"),

@@ -121,3 +121,58 @@ def test_odd_width_small_groups(act):
     e_gpu = O.reconstruction_error(W, g.W_hat, H)
     e_or = O.reconstruction_error(W, o.what, H)
     assert abs(e_gpu - e_or) <= 0.01 * e_or
+
+
+@pytest.mark.parametrize("bits,group,block", [(2, 64, 64), (8, 128, 128), (3, 512, 128),
+                                              (5, 32, 128)])
+def test_bit_widths_and_per_channel(bits, group, block):
+    """Affine grids of 2, 3, 5 and 8 bits; group = cols is one scale per row
+    (per-channel)."""
+    cfg = I.CONFIGS["down_proj_4096x11008_int4_g128_actorder"].with_(
+        rows=48, cols=512, tokens=1500, bits=bits, group=group, block=block)
+    W = I.weight(cfg)
+    store = [I.x_chunk_storage(cfg, 0, 1500)]
+    g = gpu_layer(cfg, W, store)
+    o, H, diag = oracle_layer(cfg, W.astype(np.float64), [I.bf16_to_f32(store[0])])
+    rep = classify_codes(g.q[:, o.perm], o.sweep, "affine", group)
+    log(f"[edges] bits={bits} g={group} B={block}: {rep.mismatches} code mismatches")
+    assert_codes(rep)
+    assert int(g.q.max()) <= 2 ** bits - 1
+    e_gpu = O.reconstruction_error(W, g.W_hat, H)
+    e_or = O.reconstruction_error(W, o.what, H)
+    assert abs(e_gpu - e_or) <= 0.01 * e_or
+
+
+@pytest.mark.parametrize("bits,act", [(2, False), (3, True), (5, False), (6, True)])
+def test_kquant_code_widths(bits, act):
+    """Two-level grid with 2-, 3-, 5- and 6-bit codes (sub-block scale/min
+    codes 4, 6, 6 and 8 bits wide): codes, super- and sub-block codes equal
+    the oracle's away from tie cascades, dequantized weights on the GPU's own
+    grid, reconstruction error within 1 %."""
+    from tests.parity import cascade_mask
+    cfg = I.CONFIGS["q4k_14336x4096"].with_(rows=64, cols=768, tokens=1500, bits=bits,
+                                              act_order=act)
+    W = I.weight(cfg)
+    store = [I.x_chunk_storage(cfg, 0, 1500)]
+    g = gpu_layer(cfg, W, store)
+    o, H, diag = oracle_layer(cfg, W.astype(np.float64), [I.bf16_to_f32(store[0])])
+    perm = o.perm
+    qg_p = g.q[:, perm]
+    rep = classify_codes(qg_p, o.sweep, "q4k", 256)
+    log(f"[edges] k-quant bits={bits}: {rep.mismatches} code mismatches")
+    assert_codes(rep)
+    kmax = 2 ** O.kquant_sub_bits(bits) - 1
+    assert int(g.q.max()) <= 2 ** bits - 1
+    assert int(g.sc.max()) <= kmax and int(g.mc.max()) <= kmax
+    casc = cascade_mask(qg_p, o.sweep, O.Q4K_SUPER)
+    casc_sub = np.repeat(casc, 8, axis=1)
+    np.testing.assert_array_equal(g.D[~casc], o.sweep.D[~casc])
+    np.testing.assert_array_equal(g.Dm[~casc], o.sweep.Dm[~casc])
+    np.testing.assert_array_equal(g.sc[~casc_sub], o.sweep.sc[~casc_sub])
+    np.testing.assert_array_equal(g.mc[~casc_sub], o.sweep.mc[~casc_sub])
+    S = np.repeat(np.repeat(g.D.astype(np.float32), 8, axis=1) * g.sc, 32, axis=1)
+    M = np.repeat(np.repeat(g.Dm.astype(np.float32), 8, axis=1) * g.mc, 32, axis=1)
+    np.testing.assert_array_equal(g.W_hat[:, perm], S * qg_p.astype(np.float32) - M)
+    e_gpu = O.reconstruction_error(W, g.W_hat, H)
+    e_or = O.reconstruction_error(W, o.what, H)
+    assert abs(e_gpu - e_or) <= 0.01 * e_or
