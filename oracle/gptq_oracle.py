@@ -170,6 +170,45 @@ def affine_params(v: np.ndarray, bits: int):
     return s.astype(f32), z.astype(f32), zr.astype(f32)
 
 
+# Importance-weighted grid choice (the search the gguf discussion describes:
+# "Add gguf q4_k quantization", review thread -- scales and offsets chosen to
+# minimize a weighted squared error, which covers rounding and clamping
+# error, the weights being per-channel importances from the activations).
+# Reading: the candidates share the min-max zero point and shrink the
+# min-max scale by f_k = 1 - k/32, k = 0..15, clipping both ends of the range
+# in proportion; the importance of column i is its activation energy
+# diag(H)_i; the first candidate of least weighted error is taken.
+SEARCH_SHRINK = np.array([1.0 - k / 32.0 for k in range(16)], dtype=f32)
+
+
+def affine_params_weighted(v: np.ndarray, h: np.ndarray, bits: int):
+    """Affine grid of one group for each row by importance-weighted search.
+
+    v: (rows, g) current weights of the group, h: (g,) importances.  For each
+    candidate scale s_k = f_k s0 (float32, s0 and z0 from affine_params):
+    q = clamp(rint(v / s_k) + z0, 0, maxq) and w^ = s_k (q - z0) in float32,
+    E_k = sum_i h_i (v_i - w^_i)^2 in float64.  Returns float32 (scale, zero,
+    zero before rounding) and, for each row, the relative gap between the
+    least and the next-least E_k (0 when the choice is a tie)."""
+    s0, z0, zr = affine_params(v, bits)
+    maxq = f32(2 ** bits - 1)
+    v = np.asarray(v, dtype=f32)
+    h = np.asarray(h, dtype=np.float64)
+    E = np.empty((len(SEARCH_SHRINK), v.shape[0]))
+    for k, f in enumerate(SEARCH_SHRINK):
+        s = (f * s0).astype(f32)
+        q = np.clip(np.rint(v / s[:, None]) + z0[:, None], f32(0), maxq)
+        what = (s[:, None] * (q - z0[:, None])).astype(f32)
+        d = (v - what).astype(np.float64)
+        E[k] = (h[None, :] * (d * d)).sum(axis=1)
+    best = np.argmin(E, axis=0)                    # first least error
+    s = (SEARCH_SHRINK[best] * s0).astype(f32)
+    Es = np.sort(E, axis=0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        gap = np.where(Es[0] > 0, (Es[1] - Es[0]) / Es[0], np.where(Es[1] > 0, np.inf, 0.0))
+    return s, z0, zr, gap
+
+
 def affine_quantize(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int):
     """Code and dequantized value of one column: q = clamp(rint(w/s)+z), w^ = s(q-z)."""
     maxq = f32(2 ** bits - 1)
@@ -251,6 +290,7 @@ class GridSpec:
     grid: str = "affine"   # "affine" or "q4k"
     bits: int = 4
     group: int = 128       # affine: weights per scale; q4k: 256
+    search: bool = False   # affine: importance-weighted grid choice
 
     @property
     def span(self) -> int:
@@ -266,6 +306,7 @@ class SweepResult:
     ratio: np.ndarray      # pre-rounding value of each code, float32 (rows, d)
     zratio: np.ndarray     # affine: pre-rounding zero point (rows, d/g); q4k: s_b/D
     mratio: np.ndarray     # q4k: m_b/Dm (rows, d/32); affine: unused
+    sgap: np.ndarray | None = None  # weighted search: relative gap of the choice
     D: np.ndarray | None = None
     Dm: np.ndarray | None = None
     sc: np.ndarray | None = None
@@ -275,9 +316,11 @@ class SweepResult:
 class _GroupState:
     """Grid parameters of the group (super-block) currently being quantized."""
 
-    def __init__(self, spec: GridSpec, rows: int, d: int):
+    def __init__(self, spec: GridSpec, rows: int, d: int, importance=None):
         self.spec = spec
+        self.importance = importance
         ng = d // spec.span
+        self.sgap = np.full((rows, ng), np.inf)
         if spec.grid == "affine":
             self.scale = np.zeros((rows, ng), f32)
             self.zero = np.zeros((rows, ng), f32)
@@ -298,7 +341,12 @@ class _GroupState:
         """Choose the grid of the group starting at column j from current weights v."""
         sp = self.spec
         gi = j // sp.span
-        if sp.grid == "affine":
+        if sp.grid == "affine" and sp.search:
+            h = self.importance[j:j + v.shape[1]]
+            s, z, zr, gap = affine_params_weighted(v, h, sp.bits)
+            self.scale[:, gi], self.zero[:, gi], self.zratio[:, gi] = s, z, zr
+            self.sgap[:, gi] = gap
+        elif sp.grid == "affine":
             s, z, zr = affine_params(v, sp.bits)
             self.scale[:, gi], self.zero[:, gi], self.zratio[:, gi] = s, z, zr
         else:
@@ -343,7 +391,7 @@ def _check_shapes(W, U, spec: GridSpec, block: int | None):
 
 
 def gptq_sweep(Wp: np.ndarray, U: np.ndarray, spec: GridSpec,
-               block: int | None = None) -> SweepResult:
+               block: int | None = None, importance=None) -> SweepResult:
     """Quantize Wp (rows x d, processing order) column by column.
 
     block=None is the plain definition: after column j every later column k
@@ -358,7 +406,9 @@ def gptq_sweep(Wp: np.ndarray, U: np.ndarray, spec: GridSpec,
     Q = np.zeros((r, d), f32)
     What = np.zeros((r, d), f32)
     ratio = np.zeros((r, d), f32)
-    gs = _GroupState(spec, r, d)
+    if spec.search and importance is None:
+        raise ValueError("the weighted grid search needs the columns' importances")
+    gs = _GroupState(spec, r, d, importance)
     B = d if block is None else block
     for i1 in range(0, d, B):
         i2 = min(i1 + B, d)
@@ -377,7 +427,8 @@ def gptq_sweep(Wp: np.ndarray, U: np.ndarray, spec: GridSpec,
         if block is not None and i2 < d:
             W[:, i2:] -= Err @ U[i1:i2, i2:]
     res = SweepResult(q=Q, what=What, scale=gs.scale, zero=gs.zero, ratio=ratio,
-                      zratio=gs.zratio, mratio=gs.mratio)
+                      zratio=gs.zratio, mratio=gs.mratio,
+                      sgap=gs.sgap if spec.search else None)
     if spec.grid == "q4k":
         res.D, res.Dm, res.sc, res.mc = gs.D, gs.Dm, gs.sc, gs.mc
     return res
@@ -406,11 +457,13 @@ class LayerResult:
 def quantize_layer(W: np.ndarray, H: np.ndarray, diag: np.ndarray, *, bits: int,
                    group: int, block: int | None, act_order: bool,
                    percdamp: float, grid: str = "affine", route: str = "literal",
-                   rows: np.ndarray | None = None) -> LayerResult:
+                   rows: np.ndarray | None = None, search: bool = False) -> LayerResult:
     """GPTQ on one linear layer (W rows x d, H d x d, diag = activation energy).
 
     ``rows`` restricts the sweep to a subset of W's rows (rows are independent
-    given U); W is then only those rows."""
+    given U); W is then only those rows.  ``search`` (affine grid) chooses
+    each group's grid by the importance-weighted search, the importance of a
+    column being its activation energy diag[i]."""
     W = np.asarray(W, dtype=np.float64)
     d = W.shape[1]
     diag = np.asarray(diag, dtype=np.float64)
@@ -420,8 +473,11 @@ def quantize_layer(W: np.ndarray, H: np.ndarray, diag: np.ndarray, *, bits: int,
     U = inverse_cholesky_upper(Hp) if route == "literal" else inverse_cholesky_upper_ul(Hp)
     Wd = W.copy()
     Wd[:, dead] = 0.0
-    spec = GridSpec(grid=grid, bits=bits, group=(Q4K_SUPER if grid == "q4k" else group))
-    sw = gptq_sweep(Wd[:, perm], U, spec, block)
+    if search and grid != "affine":
+        raise ValueError("the weighted grid search is defined for the affine grid")
+    spec = GridSpec(grid=grid, bits=bits, group=(Q4K_SUPER if grid == "q4k" else group),
+                    search=search)
+    sw = gptq_sweep(Wd[:, perm], U, spec, block, importance=diag[perm] if search else None)
     q = np.empty_like(sw.q)
     what = np.empty_like(sw.what)
     q[:, perm] = sw.q

@@ -464,3 +464,108 @@ def test_kquant_exact_grid_is_recovered(bits):
         q, wq = O.q4k_quantize(v[:, 32 * b:32 * b + 32], S_o[:, b:b + 1], M_o[:, b:b + 1], bits)
         np.testing.assert_array_equal(q[0], codes[b])
         np.testing.assert_array_equal(wq, v[:, 32 * b:32 * b + 32])
+
+
+# ------------------------------------------------ importance-weighted search
+def _weighted_error(v, h, s, z, bits):
+    """sum_i h_i (v_i - s (clamp(rint(v_i/s) + z) - z))^2 for one row, by loops."""
+    maxq = 2 ** bits - 1
+    e = 0.0
+    for vi, hi in zip(v, h):
+        q = min(max(np.rint(np.float32(vi) / np.float32(s)) + z, 0), maxq)
+        wq = np.float32(np.float32(s) * np.float32(q - z))
+        d = float(np.float32(np.float32(vi) - wq))
+        e += float(hi) * d * d
+    return e
+
+
+def _best_scale_bruteforce(v, h, z, bits):
+    """Least weighted error over every scale s > 0 with the zero point fixed:
+    the codes are constant between the scales at which some v_i/s crosses a
+    half-integer, and inside such an interval the error is a quadratic in s."""
+    maxq = 2 ** bits - 1
+    v = np.asarray(v, np.float64)
+    h = np.asarray(h, np.float64)
+    cuts = sorted({abs(vi) / (m + 0.5) for vi in v if vi != 0 for m in range(0, 4 * maxq)})
+    cuts = [c for c in cuts if c > 0]
+    pts = [cuts[0] / 2] + [(a + b) / 2 for a, b in zip(cuts, cuts[1:])] + [cuts[-1] * 2]
+    best = np.inf
+    for sm in pts:                           # one scale inside each interval
+        q = np.clip(np.rint(v / sm) + z, 0, maxq) - z
+        den = float((h * q * q).sum())
+        cand = [sm]
+        if den > 0:
+            cand.append(float((h * v * q).sum()) / den)   # the interval's quadratic minimum
+        for s in cand:
+            if s <= 0:
+                continue
+            qq = np.clip(np.rint(v / s) + z, 0, maxq) - z
+            if not np.array_equal(qq, q):
+                continue                     # outside this interval
+            best = min(best, float((h * (v - s * qq) ** 2).sum()))
+    return best
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_weighted_search_between_minmax_and_optimum(bits):
+    """The search's weighted error never exceeds the min-max grid's (its first
+    candidate) and never undercuts the least error over all scales (brute force
+    over every distinct rounding, same zero point)."""
+    rng = np.random.default_rng(60 + bits)
+    v = (rng.standard_normal((40, 6)) * 0.02).astype(np.float32)
+    v[::3, 0] *= 6                           # some rows with an outlier
+    h = rng.uniform(0.1, 3.0, 6)
+    s, z, _, _ = O.affine_params_weighted(v, h, bits)
+    s0, z0, _ = O.affine_params(v, bits)
+    assert np.array_equal(z, z0)
+    improved = 0
+    for r in range(v.shape[0]):
+        e = _weighted_error(v[r], h, s[r], z[r], bits)
+        e0 = _weighted_error(v[r], h, s0[r], z0[r], bits)
+        eopt = _best_scale_bruteforce(v[r], h, z[r], bits)
+        assert e <= e0 * (1 + 1e-12) + 1e-30
+        assert e >= eopt * (1 - 1e-9) - 1e-30
+        improved += e < e0 * (1 - 1e-6)
+    assert improved > 0
+
+
+def test_weighted_search_ignores_unimportant_outlier():
+    """Weights on the grid of the candidate f_3 s0 = (29/32) s0, and one outlier
+    (which alone sets the min-max range) of importance 0: the search lands on
+    that candidate with zero weighted error; with all importances 1 it does not."""
+    maxq = 15
+    target = np.float32(0.001)
+    s0 = np.float32(target / np.float32(29.0 / 32.0))
+    codes = np.array([0, 1, 3, 4, 7, 9, 11, 12], np.float32)
+    v = np.append((target * codes).astype(np.float32), np.float32(s0 * maxq))[None, :]
+    s_mm, z_mm, _ = O.affine_params(v, 4)
+    assert z_mm[0] == 0 and abs(float(s_mm[0]) / float(s0) - 1) < 1e-6
+    h = np.append(np.ones(8), 0.0)
+    s, z, _, gap = O.affine_params_weighted(v, h, 4)
+    assert float(s[0]) == float(np.float32(O.SEARCH_SHRINK[3] * s_mm[0]))
+    assert _weighted_error(v[0], h, s[0], z[0], 4) == 0.0
+    s1, _, _, _ = O.affine_params_weighted(v, np.ones(9), 4)
+    assert float(s1[0]) != float(s[0])
+
+
+def test_weighted_search_layer_invariants():
+    """With the search on, every dequantized weight still lies on its group's
+    grid, and GPTQ's error stays below plain rounding's."""
+    rng = np.random.default_rng(70)
+    W, X = rand_layer(rng, 24, 128, 400, outliers=3)
+    H, diag = O.hessian([X]), O.hessian_diag([X])
+    res = O.quantize_layer(W, H, diag, bits=4, group=32, block=32, act_order=True,
+                           percdamp=0.01, search=True)
+    sw = res.sweep
+    s = np.repeat(sw.scale, 32, axis=1)
+    z = np.repeat(sw.zero, 32, axis=1)
+    np.testing.assert_array_equal(sw.what, (s * (sw.q - z)).astype(np.float32))
+    assert sw.sgap is not None and sw.sgap.shape == sw.scale.shape
+    base = O.quantize_layer(W, H, diag, bits=4, group=32, block=32, act_order=True,
+                            percdamp=0.01)
+    e_s = O.reconstruction_error(W, res.what, H)
+    e_b = O.reconstruction_error(W, base.what, H)
+    rtn = O.rtn(W[:, res.perm], O.GridSpec("affine", 4, 32))
+    e_rtn = O.reconstruction_error(W[:, res.perm], rtn.what, H[np.ix_(res.perm, res.perm)])
+    assert e_s <= e_rtn and e_b <= e_rtn
+    assert e_s < 1.5 * e_b
