@@ -230,6 +230,8 @@ def main():
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run one plain streaming kernel of known size (read and write "
                          "1 GiB) before the steps, to scale rocprofv3 byte counters")
+    ap.add_argument("--search", action="store_true",
+                    help="choose each group's grid by the importance-weighted search")
     ap.add_argument("--w4a16", action="store_true",
                     help="measure the W4A16 product of stored 4-bit layers instead")
     ap.add_argument("--w4a16-batches", default="1,2,4,8,16,32,64")
@@ -270,7 +272,8 @@ def main():
     for w in Ws:
         w.copy_(W0)
     layer = GptqLayer(cfg.rows, cfg.cols, bits=cfg.bits, group=cfg.group, block=cfg.block,
-                      act_order=cfg.act_order, percdamp=cfg.percdamp, grid=cfg.grid, device=dev)
+                      act_order=cfg.act_order, percdamp=cfg.percdamp, grid=cfg.grid, device=dev,
+                      search=args.search)
     out = layer.alloc_outputs()
     packed_q = torch.empty((cfg.rows, cfg.cols * cfg.bits // 32), dtype=torch.int32, device=dev)
     packed_z = None
@@ -373,7 +376,7 @@ def main():
         "config": {"workload": cfg.name, "rows": cfg.rows, "cols": cfg.cols,
                    "tokens": cfg.tokens, "chunk_tokens": chunk, "bits": cfg.bits,
                    "group": cfg.group, "block": cfg.block, "act_order": cfg.act_order,
-                   "grid": cfg.grid, "percdamp": cfg.percdamp},
+                   "grid": cfg.grid, "percdamp": cfg.percdamp, "search": args.search},
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
     }
     print(json.dumps(line), flush=True)

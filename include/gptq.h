@@ -82,6 +82,13 @@ typedef struct {
   int32_t act_order; /* 0: original column order; 1: decreasing diag(H)      */
   float percdamp;    /* damping = percdamp * mean(diag H), >= 0 (0.01 usual)   */
   int32_t grid;      /* gptq_grid                                             */
+  int32_t search;    /* AFFINE only.  0: min-max grid per group; 1: the scale
+                        of least importance-weighted squared error among
+                        (1 - k/32) x the min-max scale, k = 0..15, at the
+                        min-max zero point, the importance of a column being
+                        its activation energy hdiag ("Add gguf q4_k
+                        quantization", review thread: weighted search,
+                        activation-aware importance)                          */
 } gptq_params;
 
 /* Message of the last failing call on this thread ("" if none). */
@@ -157,6 +164,9 @@ gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d,
  *  W        in/out, rows x cols float, original column order.  On return it
  *           holds the dequantized weights W^ (what the layer uses next).
  *  U, perm, dead  from gptq_prepare_hinv with the same d and params.
+ *  hdiag    the activation energy from gptq_hessian_accumulate (cols doubles,
+ *           original order); read only when params->search is 1, else may be
+ *           NULL.
  *  q        out, rows x cols bytes, codes in original column order.
  *  g_idx    out, cols int32: group of each original column (AFFINE:
  *           processing position / group; Q4K: processing position / 32).
@@ -174,7 +184,8 @@ gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d,
  */
 gptq_status gptq_quantize_layer(float *W, int64_t rows, int64_t cols,
                                 const float *U, const int32_t *perm,
-                                const uint8_t *dead, const gptq_params *p,
+                                const uint8_t *dead, const double *hdiag,
+                                const gptq_params *p,
                                 uint8_t *q, int32_t *g_idx, float *scale,
                                 uint8_t *zero, uint16_t *q4k_super_scale,
                                 uint16_t *q4k_super_min, uint8_t *q4k_sub_scale,

@@ -40,13 +40,15 @@ class NotSPDError(GptqError):
 class gptq_params(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("act_order", ctypes.c_int32),
-                ("percdamp", ctypes.c_float), ("grid", ctypes.c_int32)]
+                ("percdamp", ctypes.c_float), ("grid", ctypes.c_int32),
+                ("search", ctypes.c_int32)]
 
 
 def make_params(bits: int, group: int, block: int, act_order: bool, percdamp: float,
-                grid: str | int = "affine") -> gptq_params:
+                grid: str | int = "affine", search: bool = False) -> gptq_params:
     g = grid if isinstance(grid, int) else {"affine": GPTQ_GRID_AFFINE, "q4k": GPTQ_GRID_Q4K}[grid]
-    return gptq_params(int(bits), int(group), int(block), int(bool(act_order)), float(percdamp), g)
+    return gptq_params(int(bits), int(group), int(block), int(bool(act_order)), float(percdamp), g,
+                       int(bool(search)))
 
 
 class gptq_w4a16_layer(ctypes.Structure):
@@ -78,7 +80,7 @@ def lib() -> ctypes.CDLL:
     L.gptq_prepare_hinv.restype = I32
     L.gptq_prepare_hinv.argtypes = [P, P, I64, ctypes.POINTER(gptq_params), P, P, P, P, SZ, P]
     L.gptq_quantize_layer.restype = I32
-    L.gptq_quantize_layer.argtypes = [P, I64, I64, P, P, P, ctypes.POINTER(gptq_params),
+    L.gptq_quantize_layer.argtypes = [P, I64, I64, P, P, P, P, ctypes.POINTER(gptq_params),
                                       P, P, P, P, P, P, P, P, P, SZ, P]
     L.gptq_pack.restype = I32
     L.gptq_pack.argtypes = [P, I64, I64, I32, P, P]
@@ -159,10 +161,11 @@ def gptq_prepare_hinv(H, hdiag, params: gptq_params, U, perm, dead, ws, stream=N
 
 def gptq_quantize_layer(W, U, perm, dead, params: gptq_params, q, g_idx, scale=None, zero=None,
                         q4k_super_scale=None, q4k_super_min=None, q4k_sub_scale=None,
-                        q4k_sub_min=None, ws=None, stream=None):
+                        q4k_sub_min=None, ws=None, stream=None, hdiag=None):
     rows, cols = W.shape
     _check(lib().gptq_quantize_layer(
-        _ptr(W), rows, cols, _ptr(U), _ptr(perm), _ptr(dead), ctypes.byref(params), _ptr(q),
+        _ptr(W), rows, cols, _ptr(U), _ptr(perm), _ptr(dead), _ptr(hdiag), ctypes.byref(params),
+        _ptr(q),
         _ptr(g_idx), _ptr(scale), _ptr(zero), _ptr(q4k_super_scale), _ptr(q4k_super_min),
         _ptr(q4k_sub_scale), _ptr(q4k_sub_min), _ptr(ws), 0 if ws is None else ws.numel(),
         _stream(stream)))

@@ -122,6 +122,10 @@ static gptq_status check_params(const gptq_params *p, int64_t cols) {
     return fail(GPTQ_ERR_INVALID_ARG, "percdamp must be finite and >= 0");
   if (cols > 0 && cols % p->group != 0)
     return fail(GPTQ_ERR_INVALID_ARG, "cols must be a multiple of group");
+  if (p->search != 0 && p->search != 1)
+    return fail(GPTQ_ERR_INVALID_ARG, "search must be 0 or 1");
+  if (p->search && p->grid != GPTQ_GRID_AFFINE)
+    return fail(GPTQ_ERR_INVALID_ARG, "the weighted grid search is for the affine grid");
   return GPTQ_OK;
 }
 
@@ -192,7 +196,8 @@ gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d,
 }
 
 gptq_status gptq_quantize_layer(float *W, int64_t rows, int64_t cols, const float *U,
-                                const int32_t *perm, const uint8_t *dead, const gptq_params *p,
+                                const int32_t *perm, const uint8_t *dead, const double *hdiag,
+                                const gptq_params *p,
                                 uint8_t *q, int32_t *g_idx, float *scale, uint8_t *zero,
                                 uint16_t *q4k_super_scale, uint16_t *q4k_super_min,
                                 uint8_t *q4k_sub_scale, uint8_t *q4k_sub_min, void *ws,
@@ -202,6 +207,8 @@ gptq_status gptq_quantize_layer(float *W, int64_t rows, int64_t cols, const floa
   GPTQ_TRY(check_params(p, cols));
   if (!W || !U || !perm || !dead || !q || !g_idx)
     return fail(GPTQ_ERR_INVALID_ARG, "W, U, perm, dead, q and g_idx must not be NULL");
+  if (p->search && !hdiag)
+    return fail(GPTQ_ERR_INVALID_ARG, "the weighted grid search needs hdiag");
   if (p->grid == GPTQ_GRID_AFFINE && (!scale || !zero))
     return fail(GPTQ_ERR_INVALID_ARG, "the affine grid needs scale and zero outputs");
   if (p->grid == GPTQ_GRID_Q4K &&
@@ -212,7 +219,7 @@ gptq_status gptq_quantize_layer(float *W, int64_t rows, int64_t cols, const floa
   if (!aligned(W, 16) || !aligned(U, 16))
     return fail(GPTQ_ERR_INVALID_ARG, "W and U must be 16-byte aligned");
   GPTQ_TRY(check_ws(ws, ws_bytes, quantize_ws_bytes(rows, cols, *p)));
-  return quantize_layer_impl(W, rows, cols, U, perm, dead, *p, q, g_idx, scale, zero,
+  return quantize_layer_impl(W, rows, cols, U, perm, dead, hdiag, *p, q, g_idx, scale, zero,
                              q4k_super_scale, q4k_super_min, q4k_sub_scale, q4k_sub_min, ws,
                              ws_bytes, (hipStream_t)stream);
 }

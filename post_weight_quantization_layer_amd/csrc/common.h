@@ -89,7 +89,8 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
                               void *ws, size_t ws_bytes, hipStream_t stream);
 size_t prepare_ws_bytes(int64_t d);
 gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const float *U,
-                                const int32_t *perm, const uint8_t *dead, const gptq_params &p,
+                                const int32_t *perm, const uint8_t *dead, const double *hdiag,
+                                const gptq_params &p,
                                 uint8_t *q, int32_t *g_idx, float *scale, uint8_t *zero,
                                 uint16_t *D, uint16_t *Dm, uint8_t *sc, uint8_t *mc, void *ws,
                                 size_t ws_bytes, hipStream_t stream);

@@ -42,6 +42,8 @@ struct SweepArgs {
   int i1, B;
   int bits, group;
   int sub_bits;    // two-level grid: width of the sub-block scale/min codes
+  int search;      // affine: importance-weighted grid choice
+  const double *hp;  // search: importance of each column, processing order
   float *scale;    // affine: rows x (cols/group)
   uint8_t *zero;
   uint16_t *D, *Dm;   // q4k: rows x (cols/256)
@@ -133,6 +135,13 @@ __device__ __forceinline__ float group_max(float v) {
   for (int off = 1; off < kLPR; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
 }
+// Butterfly sum over the row's 16 lanes: every lane adds the same pairs
+// (addition commutes exactly), so all of them hold the same bits.
+__device__ __forceinline__ double group_sum(double v) {
+#pragma unroll
+  for (int off = 1; off < kLPR; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
 
 // Value of lane `sub` of this lane's 16-lane row, by a DPP row broadcast
 // (one VALU move; the source lane is an immediate).
@@ -169,6 +178,8 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
   extern __shared__ __align__(16) float Ub[];
   const int Bp = (a.B + 7) & ~7;
   float *Uinv = Ub + (Bp + 2) * kMaxB;
+  // search: the block's column importances (doubles, 8-byte aligned)
+  double *hs = reinterpret_cast<double *>(Uinv + ((Bp + 2 + 1) & ~1));
   const int tid = threadIdx.x;
   const int B = a.B;
   const int64_t ld = a.cols;
@@ -247,6 +258,8 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
     Ub[(e / (kMaxB - B)) * kMaxB + B + e % (kMaxB - B)] = 0.f;
   for (int e = tid; e < (Bp + 2 - B) * kMaxB; e += kSweepThreads) Ub[B * kMaxB + e] = 0.f;
   for (int j = B + tid; j < Bp + 2; j += kSweepThreads) Uinv[j] = 0.f;
+  if (a.search)
+    for (int c = tid; c < B; c += kSweepThreads) hs[c] = a.hp[a.i1 + c];
   __syncthreads();
 
   for (; r0 < a.rows; r0 += rows_per_pass) {
@@ -311,6 +324,41 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
             s = (xmax - xmin) / maxq;
             rs = 1.f / s;
             z = fminf(fmaxf(__builtin_rintf(-xmin / s), 0.f), maxq);
+            if (a.search) {
+              // Importance-weighted choice among the scales (1 - k/32) s,
+              // k = 0..15, at the same zero point: codes in float32 as the
+              // sweep takes them, errors h (w - w^)^2 summed in float64; the
+              // first least error wins.
+              const float s0 = s;
+              double best = INFINITY;
+              for (int k = 0; k < 16; ++k) {
+                const float sk = (1.f - float(k) * 0.03125f) * s0;
+                const float rsk = 1.f / sk;
+                double e = 0.0;
+#pragma unroll
+                for (int y = 0; y < kCPL; ++y) {
+                  const int c = c0 + y;
+                  if (c < B && c >= j && c < j + G) {
+                    const float qv =
+                        __builtin_amdgcn_fmed3f(rint_div(w[y], sk, rsk) + z, 0.f, maxq);
+                    const float d = __fsub_rn(w[y], __fmul_rn(sk, qv - z));
+                    e = fma(hs[c], double(d) * double(d), e);
+                  }
+                }
+                for (int c = B + sl; c < j + G; c += kLPR) {  // group reaches past the block
+                  const float v = wrow[c];
+                  const float qv = __builtin_amdgcn_fmed3f(rint_div(v, sk, rsk) + z, 0.f, maxq);
+                  const float d = __fsub_rn(v, __fmul_rn(sk, qv - z));
+                  e = fma(a.hp[a.i1 + c], double(d) * double(d), e);
+                }
+                e = group_sum(e);
+                if (e < best) {
+                  best = e;
+                  s = sk;
+                }
+              }
+              rs = 1.f / s;
+            }
             if (sl == 0 && rv) {
               a.scale[row * ngroups + gi] = s;
               a.zero[row * ngroups + gi] = (uint8_t)z;
@@ -651,6 +699,14 @@ __global__ void __launch_bounds__(256)
   if (p < cols) g_idx[perm[p]] = (int32_t)(p / gsz);
 }
 
+// Importance of each column in processing order: its activation energy.
+__global__ void __launch_bounds__(256)
+    importance_kernel(const double *__restrict__ hdiag, const int32_t *__restrict__ perm,
+                      int64_t cols, double *__restrict__ hp) {
+  const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (j < cols) hp[j] = hdiag[perm[j]];
+}
+
 bool g_sweep_lds_set[4] = {false, false, false, false};
 
 }  // namespace
@@ -661,11 +717,13 @@ size_t quantize_ws_bytes(int64_t rows, int64_t cols, const gptq_params &p) {
     n += align256(size_t(rows) * size_t(cols) * sizeof(float));  // Wp
     n += align256(size_t(rows) * size_t(cols));                  // qp
   }
+  if (p.search) n += align256(size_t(cols) * sizeof(double));    // importances, processing order
   return n;
 }
 
 gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const float *U,
-                                const int32_t *perm, const uint8_t *dead, const gptq_params &p,
+                                const int32_t *perm, const uint8_t *dead, const double *hdiag,
+                                const gptq_params &p,
                                 uint8_t *q, int32_t *g_idx, float *scale, uint8_t *zero,
                                 uint16_t *D, uint16_t *Dm, uint8_t *sc, uint8_t *mc, void *ws,
                                 size_t ws_bytes, hipStream_t stream) {
@@ -685,6 +743,7 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
     Wp = reinterpret_cast<float *>(base);
     base += align256(size_t(rows) * size_t(cols) * sizeof(float));
     qp = base;
+    base += align256(size_t(rows) * size_t(cols));
     if (row_lds <= 65536)
       GPTQ_TRY(launch("quant_gather", gather_cols_lds_kernel, dim3(growsn), dim3(256),
                       size_t(cols) * 4, stream, (const float *)W, rows, cols, perm, dead, Wp));
@@ -696,10 +755,20 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
                     W, rows, cols, dead));
   }
 
+  const double *hp = nullptr;
+  if (p.search) {
+    double *h = reinterpret_cast<double *>(base);
+    base += align256(size_t(cols) * sizeof(double));
+    GPTQ_TRY(launch("quant_importance", importance_kernel, dim3(cdiv(cols, 256)), dim3(256), 0,
+                    stream, hdiag, perm, cols, h));
+    hp = h;
+  }
+
   const int q4k = p.grid == GPTQ_GRID_Q4K;
   const int B = p.block;
   const size_t Bp = (B + 7) & ~7;
-  const size_t lds = ((Bp + 2) * kMaxB + Bp + 2) * sizeof(float);
+  const size_t lds = ((Bp + 2) * kMaxB + Bp + 2 + 1) * sizeof(float) +
+                     (p.search ? size_t(B) * sizeof(double) : 0);
   const int g8 = (q4k ? 256 : p.group) % 8 == 0;
   const int variant = q4k * 2 + g8;
   // (Q4_K groups are 256 columns, always a multiple of 8: variant 3)
@@ -738,6 +807,8 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   a.bits = p.bits;
   a.group = p.group;
   a.sub_bits = p.bits == 2 ? 4 : p.bits == 6 ? 8 : 6;
+  a.search = p.search;
+  a.hp = hp;
   a.scale = scale;
   a.zero = zero;
   a.D = D;

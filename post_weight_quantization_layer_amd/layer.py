@@ -34,12 +34,12 @@ class GptqLayer:
 
     def __init__(self, rows: int, cols: int, *, bits: int, group: int, block: int,
                  act_order: bool, percdamp: float = 0.01, grid: str = "affine",
-                 device: str = "cuda"):
+                 device: str = "cuda", search: bool = False):
         self.rows, self.cols = rows, cols
         self.grid = grid
         self.bits = bits
         self.group = 256 if grid == "q4k" else group
-        self.params = B.make_params(bits, self.group, block, act_order, percdamp, grid)
+        self.params = B.make_params(bits, self.group, block, act_order, percdamp, grid, search)
         dev = torch.device(device)
         self.device = dev
         self.H = torch.zeros((cols, cols), dtype=torch.float32, device=dev)
@@ -81,7 +81,7 @@ class GptqLayer:
         """W: rows x cols float32 on the device; overwritten with W^."""
         out = self.alloc_outputs() if out is None else out
         B.gptq_quantize_layer(W, self.U, self.perm, self.dead, self.params, ws=self.ws,
-                              stream=stream, **out)
+                              stream=stream, hdiag=self.hdiag, **out)
         return QuantizedLayer(q=out["q"], g_idx=out["g_idx"], W_hat=W, perm=self.perm,
                               dead=self.dead, scale=out.get("scale"), zero=out.get("zero"),
                               super_scale=out.get("q4k_super_scale"),

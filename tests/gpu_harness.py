@@ -49,13 +49,15 @@ class GpuOut:
     mc: np.ndarray | None = None
 
 
-def gpu_layer(cfg: I.LayerConfig, W: np.ndarray, chunks, dev="cuda", keep_H=True) -> GpuOut:
+def gpu_layer(cfg: I.LayerConfig, W: np.ndarray, chunks, dev="cuda", keep_H=True,
+              search=False) -> GpuOut:
     """chunks: iterable of storage-dtype X chunks (d x n_c)."""
     import torch
     from post_weight_quantization_layer_amd import binding as B
     from post_weight_quantization_layer_amd.layer import GptqLayer
     L = GptqLayer(W.shape[0], cfg.cols, bits=cfg.bits, group=cfg.group, block=cfg.block,
-                  act_order=cfg.act_order, percdamp=cfg.percdamp, grid=cfg.grid, device=dev)
+                  act_order=cfg.act_order, percdamp=cfg.percdamp, grid=cfg.grid, device=dev,
+                  search=search)
     for xs in chunks:
         t, n, ld = to_device_x(xs, dev)
         B.gptq_hessian_accumulate(L.H, L.hdiag, t, n_tok=n, ld_x=ld)
@@ -79,7 +81,7 @@ def gpu_layer(cfg: I.LayerConfig, W: np.ndarray, chunks, dev="cuda", keep_H=True
     return out
 
 
-def oracle_layer(cfg: I.LayerConfig, W: np.ndarray, chunks_f32, block=None):
+def oracle_layer(cfg: I.LayerConfig, W: np.ndarray, chunks_f32, block=None, search=False):
     H = None
     diag = None
     for xc in chunks_f32:
@@ -88,5 +90,6 @@ def oracle_layer(cfg: I.LayerConfig, W: np.ndarray, chunks_f32, block=None):
         H = h if H is None else H + h
         diag = dg if diag is None else diag + dg
     res = O.quantize_layer(W, H, diag, bits=cfg.bits, group=cfg.group, block=block,
-                           act_order=cfg.act_order, percdamp=cfg.percdamp, grid=cfg.grid)
+                           act_order=cfg.act_order, percdamp=cfg.percdamp, grid=cfg.grid,
+                           search=search)
     return res, H, diag

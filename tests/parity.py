@@ -48,12 +48,15 @@ class CodeReport:
 
 
 def classify_codes(q_gpu_p: np.ndarray, orc: "O.SweepResult", grid: str, group: int,
-                   tau: float = 1e-3) -> CodeReport:
-    """q_gpu_p: GPU codes in processing order (rows x d)."""
+                   tau: float = 1e-3, search_tau: float = 1e-9) -> CodeReport:
+    """q_gpu_p: GPU codes in processing order (rows x d).  With the weighted
+    grid search, a group whose best and next-best candidate errors lie within
+    ``search_tau`` (relative) of each other is a grid tie too."""
     qo = orc.q.astype(np.int64)
     qg = q_gpu_p.astype(np.int64)
     diff = qg != qo
     unclassified = []
+    search_rows = []
     rows = np.nonzero(diff.any(axis=1))[0]
     for r in rows:
         j0 = int(np.argmax(diff[r]))
@@ -61,6 +64,12 @@ def classify_codes(q_gpu_p: np.ndarray, orc: "O.SweepResult", grid: str, group: 
         if grid == "affine":
             g = j0 // group
             tie = tie or bool(near_half(orc.zratio[r, g], tau))
+            if orc.sgap is not None and orc.sgap[r, g] < search_tau:
+                # the weighted search's two best scales are equally good: either
+                # choice is the method's result, and codes may then differ by
+                # more than one step in that row
+                tie = True
+                search_rows.append(int(r))
         else:
             sb = j0 // O.Q4K_SUPER
             subs = slice(sb * 8, sb * 8 + 8)
@@ -69,7 +78,9 @@ def classify_codes(q_gpu_p: np.ndarray, orc: "O.SweepResult", grid: str, group: 
         if not tie:
             unclassified.append((int(r), j0, float(orc.ratio[r, j0]), int(qo[r, j0]),
                                  int(qg[r, j0])))
-    step = int(np.abs(qg - qo).max()) if diff.any() else 0
+    keep = np.ones(qo.shape[0], bool)
+    keep[search_rows] = False
+    step = int(np.abs(qg - qo)[keep].max()) if diff[keep].any() else 0
     return CodeReport(n=qo.size, mismatches=int(diff.sum()), rows_with_mismatch=len(rows),
                       unclassified=unclassified, max_step=step)
 

@@ -55,15 +55,17 @@ FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
     (dict(grid=1, bits=4, group=128), "256"),
     (dict(grid=7), "grid"),
     (dict(group=96, block=32), "multiple of group"),
+    (dict(search=2), "search"),
+    (dict(search=1, grid=1, group=256), "affine"),
 ])
 def test_quantize_rejects_bad_params(kw, msg):
     base = dict(bits=4, group=128, block=128, act_order=0, percdamp=0.01, grid=0)
     base.update(kw)
     p = B.gptq_params(base["bits"], base["group"], base["block"], base["act_order"],
-                      base["percdamp"], base["grid"])
+                      base["percdamp"], base["grid"], base.get("search", 0))
     L = B.lib()
-    st = L.gptq_quantize_layer(FAKE, 64, 1024, FAKE, FAKE, FAKE, ctypes.byref(p), FAKE, FAKE,
-                               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    st = L.gptq_quantize_layer(FAKE, 64, 1024, FAKE, FAKE, FAKE, FAKE, ctypes.byref(p), FAKE,
+                               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
     assert st == B.GPTQ_ERR_INVALID_ARG
     assert msg in B.gptq_last_error()
 
@@ -163,3 +165,14 @@ def test_w4a16_gemm_rejects_before_any_launch():
         B.GPTQ_ERR_WORKSPACE
     assert L.gptq_w4a16_gemm(ctypes.byref(lay), FAKE, 16, FAKE, FAKE, need - 1, None) == \
         B.GPTQ_ERR_WORKSPACE
+
+
+def test_weighted_search_needs_hdiag():
+    p = B.make_params(4, 128, 128, False, 0.01, search=True)
+    st = B.lib().gptq_quantize_layer(FAKE, 64, 1024, FAKE, FAKE, FAKE, None, ctypes.byref(p),
+                                     FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     1 << 30, None)
+    assert st == B.GPTQ_ERR_INVALID_ARG and "hdiag" in B.gptq_last_error()
+    rows = 1 << 20      # the sweep's share of the workspace is the larger one
+    n0 = B.gptq_workspace_bytes(rows, 1024, B.make_params(4, 128, 128, False, 0.01))
+    assert B.gptq_workspace_bytes(rows, 1024, p) >= n0 + 1024 * 8

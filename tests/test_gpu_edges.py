@@ -176,3 +176,48 @@ def test_kquant_code_widths(bits, act):
     e_gpu = O.reconstruction_error(W, g.W_hat, H)
     e_or = O.reconstruction_error(W, o.what, H)
     assert abs(e_gpu - e_or) <= 0.01 * e_or
+
+
+@pytest.mark.parametrize("bits,group,block,act", [(4, 128, 128, True), (3, 128, 64, True),
+                                                  (4, 32, 128, False), (4, 256, 128, True)])
+def test_weighted_grid_search(bits, group, block, act):
+    """Importance-weighted grid choice: codes, scales and zero points as the
+    oracle's away from tie cascades (search ties included), the GPU's weights
+    on its own grid, reconstruction error within 1 % of the oracle's and
+    below the min-max grid's."""
+    from tests.parity import cascade_mask, near_half
+    cfg = I.CONFIGS["down_proj_4096x11008_int4_g128_actorder"].with_(
+        rows=96, cols=768, tokens=1800, bits=bits, group=group, block=block, act_order=act,
+        x_kind="gauss", outlier_frac=0.01, outlier_scale=20.0)
+    W = I.weight(cfg)
+    store = [I.x_chunk_storage(cfg, 0, 1800)]
+    f32 = [I.bf16_to_f32(store[0])]
+    g = gpu_layer(cfg, W, store, search=True)
+    o, H, diag = oracle_layer(cfg, W.astype(np.float64), f32, search=True)
+    perm = o.perm
+    qg_p = g.q[:, perm]
+    rep = classify_codes(qg_p, o.sweep, "affine", group)
+    casc = cascade_mask(qg_p, o.sweep, group)
+    # a tie's cascade can move a later group's choice to another candidate,
+    # so the share of differing codes is counted outside the cascades
+    outside = (qg_p != o.sweep.q) & ~np.repeat(casc, group, axis=1)
+    log(f"[edges] search bits={bits} g={group}: {rep.mismatches} code mismatches in "
+        f"{rep.rows_with_mismatch} rows, {int(outside.sum())} outside tie cascades, "
+        f"{int((o.sweep.sgap < 1e-9).sum())} search ties")
+    assert not rep.unclassified, f"mismatches not at a tie: {rep.unclassified[:5]}"
+    assert outside.sum() == 0
+    assert rep.rows_with_mismatch <= max(1, qg_p.shape[0] // 50)
+    rel = np.abs(g.scale - o.sweep.scale) / o.sweep.scale
+    assert rel[~casc].max() <= 1e-3
+    zdiff = (g.zero.astype(np.int64) != o.sweep.zero.astype(np.int64)) & ~casc
+    assert np.all(near_half(o.sweep.zratio[zdiff], 1e-3))
+    s = np.repeat(g.scale, group, axis=1)
+    z = np.repeat(g.zero.astype(np.float32), group, axis=1)
+    np.testing.assert_array_equal(g.W_hat[:, perm], s * (qg_p.astype(np.float32) - z))
+    e_gpu = O.reconstruction_error(W, g.W_hat, H)
+    e_or = O.reconstruction_error(W, o.what, H)
+    assert abs(e_gpu - e_or) <= 0.01 * e_or
+    base = gpu_layer(cfg, W, store)
+    e_base = O.reconstruction_error(W, base.W_hat, H)
+    log(f"[edges] search bits={bits} g={group}: E_search / E_minmax = {e_gpu / e_base:.3f}")
+    assert e_gpu < e_base
