@@ -273,6 +273,62 @@ def q4k_params(v: np.ndarray, bits: int = 4):
     return D, Dm, sc.astype(np.uint8), mc.astype(np.uint8), S, M
 
 
+def q4k_params_weighted(v: np.ndarray, h: np.ndarray, bits: int = 4):
+    """Two-level grid of one super-block for each row by importance-weighted
+    search of each sub-block's scale and min, then the same second level as
+    q4k_params.
+
+    Reading (as for the affine search): for sub-block b with min-max values
+    s_b0 = (mx - mn)/maxq and m_b0 = -mn, the candidates are
+    (s, m) = (f_k s_b0, f_k m_b0), f_k = 1 - k/32, k = 0..15, both float32;
+    q = clamp(rint((v + m)/s), 0, maxq) and w^ = s q - m in float32;
+    E_k = sum_i h_i (v_i - w^_i)^2 in float64; the first least E_k gives the
+    sub-block's (s_b, m_b), from which D, Dm, sc, mc follow as in q4k_params.
+    Returns those six arrays and the relative gap of each sub-block's choice
+    (rows, 8)."""
+    maxq = f32(2 ** bits - 1)
+    kmax = f32(2 ** kquant_sub_bits(bits) - 1)
+    v = np.asarray(v, dtype=f32)
+    h = np.asarray(h, dtype=np.float64)
+    rows = v.shape[0]
+    nb = Q4K_SUPER // Q4K_SUB
+    vb = v.reshape(rows, nb, Q4K_SUB)
+    hb = h.reshape(nb, Q4K_SUB)
+    mn = np.minimum(vb.min(axis=2), f32(0))
+    mx = np.maximum(vb.max(axis=2), f32(0))
+    s0 = (mx - mn) / maxq
+    m0 = -mn
+    E = np.empty((len(SEARCH_SHRINK), rows, nb))
+    for k, f in enumerate(SEARCH_SHRINK):
+        s = (f * s0).astype(f32)
+        m = (f * m0).astype(f32)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = np.where(s[..., None] > 0,
+                         np.clip(np.rint((vb + m[..., None]) / s[..., None]), f32(0), maxq),
+                         f32(0)).astype(f32)
+        what = ((s[..., None] * q).astype(f32) - m[..., None]).astype(f32)
+        d = (vb - what).astype(np.float64)
+        E[k] = (hb[None, :, :] * (d * d)).sum(axis=2)
+    best = np.argmin(E, axis=0)
+    s_b = (SEARCH_SHRINK[best] * s0).astype(f32)
+    m_b = (SEARCH_SHRINK[best] * m0).astype(f32)
+    Es = np.sort(E, axis=0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        gap = np.where(Es[0] > 0, (Es[1] - Es[0]) / Es[0], np.where(Es[1] > 0, np.inf, 0.0))
+    D = (s_b.max(axis=1) / kmax).astype(np.float16)
+    Dm = (m_b.max(axis=1) / kmax).astype(np.float16)
+    Df = D.astype(f32)[:, None]
+    Dmf = Dm.astype(f32)[:, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sc = np.where((s_b > 0) & (Df > 0), np.clip(np.rint(s_b / Df), 1, kmax), 0)
+        mc = np.where(Dmf > 0, np.clip(np.rint(m_b / Dmf), 0, kmax), 0)
+    sc = sc.astype(f32)
+    mc = mc.astype(f32)
+    S = (Df * sc).astype(f32)
+    M = (Dmf * mc).astype(f32)
+    return D, Dm, sc.astype(np.uint8), mc.astype(np.uint8), S, M, s_b, m_b, gap
+
+
 def q4k_quantize(w: np.ndarray, S: np.ndarray, M: np.ndarray, bits: int = 4):
     """q = clamp(rint((w + M)/S), 0, 2^bits - 1) (0 when S = 0), w^ = S q - M."""
     w = np.asarray(w, dtype=f32)
@@ -290,7 +346,7 @@ class GridSpec:
     grid: str = "affine"   # "affine" or "q4k"
     bits: int = 4
     group: int = 128       # affine: weights per scale; q4k: 256
-    search: bool = False   # affine: importance-weighted grid choice
+    search: bool = False   # importance-weighted grid choice
 
     @property
     def span(self) -> int:
@@ -306,7 +362,8 @@ class SweepResult:
     ratio: np.ndarray      # pre-rounding value of each code, float32 (rows, d)
     zratio: np.ndarray     # affine: pre-rounding zero point (rows, d/g); q4k: s_b/D
     mratio: np.ndarray     # q4k: m_b/Dm (rows, d/32); affine: unused
-    sgap: np.ndarray | None = None  # weighted search: relative gap of the choice
+    sgap: np.ndarray | None = None  # weighted search: relative gap of each choice
+                                    # (affine: per group; q4k: per sub-block)
     D: np.ndarray | None = None
     Dm: np.ndarray | None = None
     sc: np.ndarray | None = None
@@ -336,6 +393,7 @@ class _GroupState:
             self.Dm = np.zeros((rows, ng), np.float16)
             self.sc = np.zeros((rows, nsub), np.uint8)
             self.mc = np.zeros((rows, nsub), np.uint8)
+            self.subgap = np.full((rows, nsub), np.inf)
 
     def choose(self, j: int, v: np.ndarray):
         """Choose the grid of the group starting at column j from current weights v."""
@@ -350,19 +408,25 @@ class _GroupState:
             s, z, zr = affine_params(v, sp.bits)
             self.scale[:, gi], self.zero[:, gi], self.zratio[:, gi] = s, z, zr
         else:
-            D, Dm, sc, mc, S, M = q4k_params(v, sp.bits)
             b0 = j // Q4K_SUB
             nb = Q4K_SUPER // Q4K_SUB
+            if sp.search:
+                h = self.importance[j:j + v.shape[1]]
+                D, Dm, sc, mc, S, M, s_b, m_b, gap = q4k_params_weighted(v, h, sp.bits)
+                self.subgap[:, b0:b0 + nb] = gap
+            else:
+                D, Dm, sc, mc, S, M = q4k_params(v, sp.bits)
+                vb = np.asarray(v, f32).reshape(v.shape[0], nb, Q4K_SUB)
+                mn = np.minimum(vb.min(axis=2), f32(0))
+                mx = np.maximum(vb.max(axis=2), f32(0))
+                s_b = (mx - mn) / f32(2 ** sp.bits - 1)
+                m_b = -mn
             self.D[:, gi], self.Dm[:, gi] = D, Dm
             self.sc[:, b0:b0 + nb], self.mc[:, b0:b0 + nb] = sc, mc
             self.scale[:, b0:b0 + nb], self.zero[:, b0:b0 + nb] = S, M
-            vb = np.asarray(v, f32).reshape(v.shape[0], nb, Q4K_SUB)
-            mn = np.minimum(vb.min(axis=2), f32(0))
-            mx = np.maximum(vb.max(axis=2), f32(0))
-            s_b = (mx - mn) / f32(2 ** sp.bits - 1)
             with np.errstate(divide="ignore", invalid="ignore"):
                 self.zratio[:, b0:b0 + nb] = s_b / D.astype(f32)[:, None]
-                self.mratio[:, b0:b0 + nb] = (-mn) / Dm.astype(f32)[:, None]
+                self.mratio[:, b0:b0 + nb] = m_b / Dm.astype(f32)[:, None]
 
     def quantize(self, j: int, w: np.ndarray):
         sp = self.spec
@@ -426,9 +490,11 @@ def gptq_sweep(Wp: np.ndarray, U: np.ndarray, spec: GridSpec,
             W[:, j] = what
         if block is not None and i2 < d:
             W[:, i2:] -= Err @ U[i1:i2, i2:]
+    sgap = None
+    if spec.search:   # per group (affine) or per sub-block (two-level grid)
+        sgap = gs.sgap if spec.grid == "affine" else gs.subgap
     res = SweepResult(q=Q, what=What, scale=gs.scale, zero=gs.zero, ratio=ratio,
-                      zratio=gs.zratio, mratio=gs.mratio,
-                      sgap=gs.sgap if spec.search else None)
+                      zratio=gs.zratio, mratio=gs.mratio, sgap=sgap)
     if spec.grid == "q4k":
         res.D, res.Dm, res.sc, res.mc = gs.D, gs.Dm, gs.sc, gs.mc
     return res
@@ -461,9 +527,9 @@ def quantize_layer(W: np.ndarray, H: np.ndarray, diag: np.ndarray, *, bits: int,
     """GPTQ on one linear layer (W rows x d, H d x d, diag = activation energy).
 
     ``rows`` restricts the sweep to a subset of W's rows (rows are independent
-    given U); W is then only those rows.  ``search`` (affine grid) chooses
-    each group's grid by the importance-weighted search, the importance of a
-    column being its activation energy diag[i]."""
+    given U); W is then only those rows.  ``search`` chooses each group's
+    (affine) or sub-block's (two-level) grid by the importance-weighted
+    search, the importance of a column being its activation energy diag[i]."""
     W = np.asarray(W, dtype=np.float64)
     d = W.shape[1]
     diag = np.asarray(diag, dtype=np.float64)
@@ -473,8 +539,6 @@ def quantize_layer(W: np.ndarray, H: np.ndarray, diag: np.ndarray, *, bits: int,
     U = inverse_cholesky_upper(Hp) if route == "literal" else inverse_cholesky_upper_ul(Hp)
     Wd = W.copy()
     Wd[:, dead] = 0.0
-    if search and grid != "affine":
-        raise ValueError("the weighted grid search is defined for the affine grid")
     spec = GridSpec(grid=grid, bits=bits, group=(Q4K_SUPER if grid == "q4k" else group),
                     search=search)
     sw = gptq_sweep(Wd[:, perm], U, spec, block, importance=diag[perm] if search else None)

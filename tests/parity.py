@@ -75,6 +75,9 @@ def classify_codes(q_gpu_p: np.ndarray, orc: "O.SweepResult", grid: str, group: 
             subs = slice(sb * 8, sb * 8 + 8)
             tie = tie or bool(near_half(orc.zratio[r, subs], tau).any()) \
                 or bool(near_half(orc.mratio[r, subs], tau).any())
+            if orc.sgap is not None and (orc.sgap[r, subs] < search_tau).any():
+                tie = True
+                search_rows.append(int(r))
         if not tie:
             unclassified.append((int(r), j0, float(orc.ratio[r, j0]), int(qo[r, j0]),
                                  int(qg[r, j0])))

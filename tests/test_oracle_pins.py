@@ -569,3 +569,97 @@ def test_weighted_search_layer_invariants():
     e_rtn = O.reconstruction_error(W[:, res.perm], rtn.what, H[np.ix_(res.perm, res.perm)])
     assert e_s <= e_rtn and e_b <= e_rtn
     assert e_s < 1.5 * e_b
+
+
+def _q4k_sub_error(v, h, s, m, bits):
+    """Weighted error of one sub-block on the grid (s, m), by loops in float32."""
+    maxq = 2 ** bits - 1
+    e = 0.0
+    for vi, hi in zip(v, h):
+        q = min(max(np.rint(np.float32(np.float32(vi) + np.float32(m)) / np.float32(s)), 0), maxq)
+        wq = np.float32(np.float32(np.float32(s) * np.float32(q)) - np.float32(m))
+        d = float(np.float32(np.float32(vi) - wq))
+        e += float(hi) * d * d
+    return e
+
+
+def _q4k_best_shrink_bruteforce(v, h, s0, m0, bits):
+    """Least weighted error over every shrink f in (0, 1] of the sub-block's
+    min-max (scale, min) = (f s0, f m0): the codes only change where
+    (v + f m0)/(f s0) crosses a half-integer, and between those points the
+    error is a quadratic in f."""
+    maxq = 2 ** bits - 1
+    v = np.asarray(v, np.float64)
+    h = np.asarray(h, np.float64)
+    cuts = set()
+    for vi in v:
+        for n in range(maxq + 1):
+            den = (n + 0.5) * s0 - m0
+            if den != 0 and vi / den > 0:
+                cuts.add(vi / den)
+    cuts = sorted(c for c in cuts if 0 < c < 1) + [1.0]
+    lo = [cuts[0] / 2] + [(a + b) / 2 for a, b in zip(cuts, cuts[1:])]
+    best = np.inf
+    for fm in lo + [1.0]:
+        q = np.clip(np.rint((v + fm * m0) / (fm * s0)), 0, maxq)
+        a = s0 * q - m0
+        cand = [fm]
+        if (h * a * a).sum() > 0:
+            cand.append(float((h * v * a).sum() / (h * a * a).sum()))
+        for f in cand:
+            if not 0 < f <= 1:
+                continue
+            qq = np.clip(np.rint((v + f * m0) / (f * s0)), 0, maxq)
+            if not np.array_equal(qq, q):
+                continue
+            best = min(best, float((h * (v - f * (s0 * qq - m0)) ** 2).sum()))
+    return best
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_q4k_weighted_search_between_minmax_and_optimum(bits):
+    """Each sub-block's searched (scale, min) has a weighted error no larger
+    than the min-max pair's (the first candidate) and no smaller than the best
+    shrink of that pair found by brute force."""
+    rng = np.random.default_rng(80 + bits)
+    v = (rng.standard_normal((6, 256)) * 0.02).astype(np.float32)
+    v[:, ::37] *= 5
+    h = rng.uniform(0.1, 3.0, 256)
+    out = O.q4k_params_weighted(v, h, bits)
+    s_b, m_b = out[6], out[7]
+    maxq = 2 ** bits - 1
+    improved = 0
+    for r in range(v.shape[0]):
+        for b in range(8):
+            vb, hb = v[r, 32 * b:32 * b + 32], h[32 * b:32 * b + 32]
+            mn, mx = min(vb.min(), 0.0), max(vb.max(), 0.0)
+            s0 = np.float32(np.float32(mx - mn) / np.float32(maxq))
+            m0 = np.float32(-mn)
+            e = _q4k_sub_error(vb, hb, s_b[r, b], m_b[r, b], bits)
+            e0 = _q4k_sub_error(vb, hb, s0, m0, bits)
+            eopt = _q4k_best_shrink_bruteforce(vb, hb, float(s0), float(m0), bits)
+            assert e <= e0 * (1 + 1e-12) + 1e-30
+            assert e >= eopt * (1 - 1e-6) - 1e-30
+            improved += e < e0 * (1 - 1e-6)
+    assert improved > 0
+
+
+def test_q4k_weighted_search_layer_invariants():
+    rng = np.random.default_rng(90)
+    W, X = rand_layer(rng, 12, 512, 900, outliers=4)
+    H, diag = O.hessian([X]), O.hessian_diag([X])
+    res = O.quantize_layer(W, H, diag, bits=4, group=256, block=128, act_order=True,
+                           percdamp=0.01, grid="q4k", search=True)
+    sw = res.sweep
+    D = np.repeat(sw.D.astype(np.float32), 8, axis=1)
+    Dm = np.repeat(sw.Dm.astype(np.float32), 8, axis=1)
+    S = np.repeat(D * sw.sc, 32, axis=1)
+    M = np.repeat(Dm * sw.mc, 32, axis=1)
+    np.testing.assert_array_equal(sw.what, (S * sw.q - M).astype(np.float32))
+    assert sw.sgap.shape == sw.sc.shape
+    base = O.quantize_layer(W, H, diag, bits=4, group=256, block=128, act_order=True,
+                            percdamp=0.01, grid="q4k")
+    rtn = O.rtn(W[:, res.perm], O.GridSpec("q4k", 4, 256))
+    e_rtn = O.reconstruction_error(W[:, res.perm], rtn.what, H[np.ix_(res.perm, res.perm)])
+    assert O.reconstruction_error(W, res.what, H) <= e_rtn
+    assert O.reconstruction_error(W, base.what, H) <= e_rtn
