@@ -82,13 +82,16 @@ typedef struct {
   int32_t act_order; /* 0: original column order; 1: decreasing diag(H)      */
   float percdamp;    /* damping = percdamp * mean(diag H), >= 0 (0.01 usual)   */
   int32_t grid;      /* gptq_grid                                             */
-  int32_t search;    /* AFFINE only.  0: min-max grid per group; 1: the scale
-                        of least importance-weighted squared error among
-                        (1 - k/32) x the min-max scale, k = 0..15, at the
-                        min-max zero point, the importance of a column being
-                        its activation energy hdiag ("Add gguf q4_k
-                        quantization", review thread: weighted search,
-                        activation-aware importance)                          */
+  int32_t search;    /* 0: min-max grids.  1: importance-weighted search,
+                        the importance of a column being its activation
+                        energy hdiag ("Add gguf q4_k quantization", review
+                        thread: weighted search, activation-aware
+                        importance).  AFFINE: the group's scale of least
+                        weighted squared error among (1 - k/32) x the min-max
+                        scale, k = 0..15, at the min-max zero point.  Q4K:
+                        each sub-block's (scale, min) among (1 - k/32) x its
+                        min-max pair, before the super-block level codes
+                        them.                                                 */
 } gptq_params;
 
 /* Message of the last failing call on this thread ("" if none). */

@@ -124,8 +124,6 @@ static gptq_status check_params(const gptq_params *p, int64_t cols) {
     return fail(GPTQ_ERR_INVALID_ARG, "cols must be a multiple of group");
   if (p->search != 0 && p->search != 1)
     return fail(GPTQ_ERR_INVALID_ARG, "search must be 0 or 1");
-  if (p->search && p->grid != GPTQ_GRID_AFFINE)
-    return fail(GPTQ_ERR_INVALID_ARG, "the weighted grid search is for the affine grid");
   return GPTQ_OK;
 }
 

@@ -387,6 +387,39 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
               mx = fmaxf(mx, 0.f);
               sb_s[t] = (mx - mn) / maxq;
               sb_m[t] = -mn;
+              if (a.search) {
+                // importance-weighted choice of the sub-block's (scale, min)
+                // among (1 - k/32) x the min-max pair, k = 0..15: codes in
+                // float32, errors in float64 over the sub-block's 4 lanes
+                // (butterfly: the same bits in all of them), first least wins
+                const float s0 = sb_s[t], m0 = sb_m[t];
+                double best = INFINITY;
+                for (int k = 0; k < 16; ++k) {
+                  const float f = 1.f - float(k) * 0.03125f;
+                  const float sk = f * s0, mk = f * m0;
+                  const float rsk = 1.f / sk;
+                  double e = 0.0;
+#pragma unroll
+                  for (int y = 0; y < kCPL; ++y) {
+                    const int p = 128 * t + c0 + y;
+                    const float v = (p < B) ? w[y] : wrow[p];
+                    const double hv = (p < B) ? hs[p] : a.hp[a.i1 + p];
+                    const float qv =
+                        sk > 0.f
+                            ? __builtin_amdgcn_fmed3f(rint_div(__fadd_rn(v, mk), sk, rsk), 0.f, maxq)
+                            : 0.f;
+                    const float d = __fsub_rn(v, __fsub_rn(__fmul_rn(sk, qv), mk));
+                    e = fma(hv, double(d) * double(d), e);
+                  }
+                  e += __shfl_xor(e, 1);
+                  e += __shfl_xor(e, 2);
+                  if (e < best) {
+                    best = e;
+                    sb_s[t] = sk;
+                    sb_m[t] = mk;
+                  }
+                }
+              }
               smax = fmaxf(smax, sb_s[t]);
               mmax = fmaxf(mmax, sb_m[t]);
             }

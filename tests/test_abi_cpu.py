@@ -56,7 +56,6 @@ FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
     (dict(grid=7), "grid"),
     (dict(group=96, block=32), "multiple of group"),
     (dict(search=2), "search"),
-    (dict(search=1, grid=1, group=256), "affine"),
 ])
 def test_quantize_rejects_bad_params(kw, msg):
     base = dict(bits=4, group=128, block=128, act_order=0, percdamp=0.01, grid=0)

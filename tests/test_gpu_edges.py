@@ -221,3 +221,47 @@ def test_weighted_grid_search(bits, group, block, act):
     e_base = O.reconstruction_error(W, base.W_hat, H)
     log(f"[edges] search bits={bits} g={group}: E_search / E_minmax = {e_gpu / e_base:.3f}")
     assert e_gpu < e_base
+
+
+@pytest.mark.parametrize("bits,act", [(4, True), (3, False)])
+def test_weighted_search_two_level_grid(bits, act):
+    """Importance-weighted (scale, min) of each sub-block of the two-level grid:
+    codes and grid codes as the oracle's outside tie cascades (search ties
+    included), weights on the GPU's own grid, reconstruction error within 1 %
+    of the oracle's and below the min-max grids'."""
+    from tests.parity import cascade_mask
+    cfg = I.CONFIGS["q4k_14336x4096"].with_(rows=80, cols=768, tokens=1600, bits=bits,
+                                              act_order=act, outlier_frac=0.01,
+                                              outlier_scale=20.0)
+    W = I.weight(cfg)
+    store = [I.x_chunk_storage(cfg, 0, 1600)]
+    f32 = [I.bf16_to_f32(store[0])]
+    g = gpu_layer(cfg, W, store, search=True)
+    o, H, diag = oracle_layer(cfg, W.astype(np.float64), f32, search=True)
+    perm = o.perm
+    qg_p = g.q[:, perm]
+    rep = classify_codes(qg_p, o.sweep, "q4k", 256)
+    casc = cascade_mask(qg_p, o.sweep, O.Q4K_SUPER)
+    outside = (qg_p != o.sweep.q) & ~np.repeat(casc, O.Q4K_SUPER, axis=1)
+    log(f"[edges] two-level search bits={bits}: {rep.mismatches} code mismatches in "
+        f"{rep.rows_with_mismatch} rows, {int(outside.sum())} outside tie cascades")
+    assert not rep.unclassified, f"mismatches not at a tie: {rep.unclassified[:5]}"
+    assert outside.sum() == 0
+    assert rep.rows_with_mismatch <= max(1, qg_p.shape[0] // 50)
+    # super-scales within one fp16 step: the searched sub-block scales carry
+    # the last-bit differences of the fp32 trailing updates, which can move
+    # max_b s_b / kmax across an fp16 rounding boundary
+    for a_, b_ in ((g.D, o.sweep.D), (g.Dm, o.sweep.Dm)):
+        ga, ob = a_[~casc].astype(np.float32), b_[~casc].astype(np.float32)
+        assert np.all(np.abs(ga - ob) <= 2.0 ** -10 * np.abs(ob))
+    same = np.repeat((g.D == o.sweep.D) & (g.Dm == o.sweep.Dm) & ~casc, 8, axis=1)
+    np.testing.assert_array_equal(g.sc[same], o.sweep.sc[same])
+    np.testing.assert_array_equal(g.mc[same], o.sweep.mc[same])
+    S = np.repeat(np.repeat(g.D.astype(np.float32), 8, axis=1) * g.sc, 32, axis=1)
+    M = np.repeat(np.repeat(g.Dm.astype(np.float32), 8, axis=1) * g.mc, 32, axis=1)
+    np.testing.assert_array_equal(g.W_hat[:, perm], S * qg_p.astype(np.float32) - M)
+    e_gpu = O.reconstruction_error(W, g.W_hat, H)
+    e_or = O.reconstruction_error(W, o.what, H)
+    assert abs(e_gpu - e_or) <= 0.01 * e_or
+    base = gpu_layer(cfg, W, store)
+    assert e_gpu < O.reconstruction_error(W, base.W_hat, H)
