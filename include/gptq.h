@@ -212,6 +212,39 @@ gptq_status gptq_quantize_layer(float *W, int64_t rows, int64_t cols,
 gptq_status gptq_pack(const uint8_t *codes, int64_t rows, int64_t cols,
                       int32_t bits, uint32_t *packed, void *stream);
 
+/* ------------------------------------------------- sequential calibration
+ * Outputs of a quantized layer, made with its updated weight, become the next
+ * layer's calibration inputs ("GPTQ implementation with tensor subclasses",
+ * section Background: for each linear, track its activations, update its
+ * weight, use the updated weight to generate its outputs, then go on to the
+ * next linear).  Activations keep the layout gptq_hessian_accumulate reads:
+ * features x tokens, bf16 bit patterns, tokens contiguous.
+ */
+
+/* Scratch bytes of gptq_linear_forward (0 on invalid sizes). */
+size_t gptq_linear_forward_ws_bytes(int64_t rows, int64_t cols, int64_t n_tok);
+
+/*
+ * Y = bf16(W X): W rows x cols float (e.g. W^ as gptq_quantize_layer leaves
+ * it), X cols x n_tok bf16 (row stride ld_x), Y rows x n_tok bf16 (row
+ * stride ld_y).  Products and sums in float32 (bf16 inputs widen exactly),
+ * one rounding to bf16 (nearest, ties to even) per output.  ws >=
+ * gptq_linear_forward_ws_bytes, 256-byte aligned.  n_tok = 0 is a no-op.
+ */
+gptq_status gptq_linear_forward(const float *W, int64_t rows, int64_t cols,
+                                const uint16_t *X, int64_t n_tok, int64_t ld_x,
+                                uint16_t *Y, int64_t ld_y, void *ws,
+                                size_t ws_bytes, void *stream);
+
+/*
+ * A = bf16(silu(G) * U) elementwise, silu(g) = g / (1 + e^-g), in float32:
+ * the gated activation between a gated MLP's gate/up linears and its down
+ * linear.  G, U rows x n_tok bf16 with row stride ld; A with row stride ld_a.
+ */
+gptq_status gptq_silu_mul(const uint16_t *G, const uint16_t *U, int64_t rows,
+                          int64_t n_tok, int64_t ld, uint16_t *A, int64_t ld_a,
+                          void *stream);
+
 /* ------------------------------------------------------------------ W4A16
  * Running the stored layer: y = x W^T, with W^ rebuilt from 4-bit codes,
  * per-group scale and zero inside the product kernel, activations in fp16

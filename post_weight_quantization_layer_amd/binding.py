@@ -23,7 +23,8 @@ EXPORTED = (
     "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_pack",
     "gptq_profile_enable", "gptq_profile_reset", "gptq_profile_query",
     "gptq_w4a16_layer_bytes", "gptq_w4a16_prepare", "gptq_w4a16_workspace_bytes",
-    "gptq_w4a16_gemm",
+    "gptq_w4a16_gemm", "gptq_linear_forward_ws_bytes", "gptq_linear_forward",
+    "gptq_silu_mul",
 )
 
 
@@ -100,6 +101,12 @@ def lib() -> ctypes.CDLL:
     L.gptq_w4a16_workspace_bytes.argtypes = [ctypes.POINTER(gptq_w4a16_layer), I64]
     L.gptq_w4a16_gemm.restype = I32
     L.gptq_w4a16_gemm.argtypes = [ctypes.POINTER(gptq_w4a16_layer), P, I64, P, P, SZ, P]
+    L.gptq_linear_forward_ws_bytes.restype = SZ
+    L.gptq_linear_forward_ws_bytes.argtypes = [I64, I64, I64]
+    L.gptq_linear_forward.restype = I32
+    L.gptq_linear_forward.argtypes = [P, I64, I64, P, I64, I64, P, I64, P, SZ, P]
+    L.gptq_silu_mul.restype = I32
+    L.gptq_silu_mul.argtypes = [P, P, I64, I64, I64, P, I64, P]
     _lib = L
     return L
 
@@ -207,6 +214,28 @@ def gptq_w4a16_gemm(layer: gptq_w4a16_layer, x, y, ws=None, batch: int | None = 
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gptq_w4a16_gemm(ctypes.byref(layer), _ptr(x), b, _ptr(y), _ptr(ws), nbytes,
                                  _stream(stream)))
+
+
+def gptq_linear_forward_ws_bytes(rows: int, cols: int, n_tok: int) -> int:
+    return lib().gptq_linear_forward_ws_bytes(rows, cols, n_tok)
+
+
+def gptq_linear_forward(W, X, Y, ws, n_tok: int | None = None, ld_x: int | None = None,
+                        ld_y: int | None = None, stream=None):
+    """W rows x cols float32, X cols x n bf16, Y rows x n bf16 (device tensors)."""
+    rows, cols = W.shape
+    n = X.shape[1] if n_tok is None else n_tok
+    _check(lib().gptq_linear_forward(
+        _ptr(W), rows, cols, _ptr(X), n, X.stride(0) if ld_x is None else ld_x, _ptr(Y),
+        Y.stride(0) if ld_y is None else ld_y, _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def gptq_silu_mul(G, U, A, n_tok: int | None = None, stream=None):
+    rows = G.shape[0]
+    n = G.shape[1] if n_tok is None else n_tok
+    _check(lib().gptq_silu_mul(_ptr(G), _ptr(U), rows, n, G.stride(0), _ptr(A), A.stride(0),
+                               _stream(stream)))
 
 
 def gptq_profile_enable(on: bool = True):

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgptq_mi355x.so")
 SOURCES = ["abi.hip", "hessian.hip", "gemm.hip", "prepare.hip", "sweep.hip", "pack.hip",
-           "w4a16.hip"]
+           "w4a16.hip", "forward.hip"]
 ARCH = "gfx950"
 
 
