@@ -275,10 +275,11 @@ __device__ inline h8_t dequant8(uint32_t w, uint32_t nz1, uint32_t nz2, const Dq
 }
 
 // Grid: tiles x splits workgroups of 4 waves.  A workgroup owns 16 * kNT * 4
-// rows and one range of steps; its waves take kNT 16-row tiles each and share
-// the range's activations, staged once in LDS.  MT 16-row slabs of x.  SPS
-// scale units per step: 1 for group >= 128, 2 for group 64, 4 for group 32.
-// NS >= the steps of any split (2, 4 or 8).
+// rows and one range of steps, walked in chunks of at most ns_max steps; its
+// waves take kNT 16-row tiles each and share each chunk's activations,
+// staged in LDS.  MT 16-row slabs of x.  SPS scale units per step: 1 for
+// group >= 128, 2 for group 64, 4 for group 32.  NS >= the steps of a chunk
+// (2, 4 or 8).
 template <int MT, int SPS, int NS>
 __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(W4Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -286,15 +287,12 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(W4Args a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kg = lane >> 4;
   const int tile = blockIdx.x / a.splits, split = blockIdx.x - tile * a.splits;
-  const int k0 = split * a.base + min(split, a.rem);
-  const int ns = a.base + (split < a.rem ? 1 : 0);
+  const int kbeg = split * a.base + min(split, a.rem);  // this split's steps:
+  const int nsplit = a.base + (split < a.rem ? 1 : 0);  //   [kbeg, kbeg + nsplit)
   const int rt0 = (tile * kWaves + wave) * kNT;
   const int row_h = a.ns_max * kStep + 8;  // LDS row stride in halves (+16 B)
   uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
 
-  // ---- weights, scales and zeros of every step of the range, issued at once
-  // (slots past the range repeat its last step: same cache lines, no branch,
-  // so the compiler can count the loads in flight exactly)
   u4_t wb[NS][kNT];
   float sb[NS][kNT][SPS];
   uint32_t zb[NS][kNT][SPS];
@@ -312,42 +310,6 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(W4Args a) {
     }
   };
 
-  // ---- stage this range of x (rows >= batch and columns >= cols are zero)
-  {
-    constexpr int kChunks = MT * NS;   // >= 16 MT rows x (16 ns) chunks / 256 threads
-    const int cpr = ns * (kStep / 8);  // 16-byte chunks per row, 16..128
-    const int db = kThreads / cpr, dc = kThreads - db * cpr;
-    int b0 = tid / cpr, c0 = tid - b0 * cpr;
-    int bs[kChunks], cs[kChunks];
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      bs[i] = b0;
-      cs[i] = c0;
-      b0 += db;
-      c0 += dc;
-      if (c0 >= cpr) {
-        c0 -= cpr;
-        ++b0;
-      }
-    }
-    u4_t stg[kChunks];
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int col = k0 * kStep + cs[i] * 8;
-      stg[i] = u4_t{0, 0, 0, 0};
-      if (bs[i] < a.batch && col < a.cols)
-        stg[i] = *reinterpret_cast<const u4_t *>(a.x + bs[i] * a.ldx + col);
-    }
-    // weights after x: loads complete in order, so x can be stored to LDS
-    // while the weights are still on their way
-#pragma unroll
-    for (int p = 0; p < NS; ++p) issue(p, k0 + min(p, ns - 1));
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i)
-      if (bs[i] < 16 * MT) *reinterpret_cast<u4_t *>(xs + bs[i] * row_h + cs[i] * 8) = stg[i];
-  }
-  __syncthreads();
-
   f4_t yacc[MT][kNT];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
@@ -356,42 +318,89 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(W4Args a) {
 
   const uint16_t *xa = xs + n * row_h + 8 * kg;  // lane's A row (m = n) and k offset
   const DqConst dq = dq_const();
-  // One step: 4 MFMA sub-steps per slab and tile; the scale of each unit is
-  // applied to the unit's fp32 sum.
-  auto step = [&](const int p) {
-    const int s = p;
-    f4_t acc[MT][kNT];
+
+  // The split's steps are walked in chunks of at most a.ns_max (<= NS):
+  // each chunk stages its x in LDS and issues all of its weights at once.
+  for (int c = 0; c < nsplit; c += a.ns_max) {
+    const int k0 = kbeg + c;
+    const int ns = min(a.ns_max, nsplit - c);
+    if (c > 0) __syncthreads();  // every wave is done with the previous chunk's x
+
+    // ---- stage this chunk of x (rows >= batch and columns >= cols are zero)
+    {
+      constexpr int kChunks = MT * NS;   // >= 16 MT rows x (16 ns) chunks / 256 threads
+      const int cpr = ns * (kStep / 8);  // 16-byte chunks per row, 16..128
+      const int db = kThreads / cpr, dc = kThreads - db * cpr;
+      int b0 = tid / cpr, c0 = tid - b0 * cpr;
+      int bs[kChunks], cs[kChunks];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      h8_t A[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        A[m] = *reinterpret_cast<const h8_t *>(xa + m * 16 * row_h + s * kStep + 32 * t);
-      const int u = t / kSub;
-#pragma unroll
-      for (int j = 0; j < kNT; ++j) {
-        const uint32_t z = (zb[p][j][u] >> (4 * (n & 7))) & 15u;
-        const uint32_t nz1 = (0xE400u | z) * 0x00010001u;
-        const uint32_t nz2 = (0xD400u | (z << 4)) * 0x00010001u;
-        const h8_t B = dequant8(wb[p][j][t], nz1, nz2, dq);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const f4_t c0 = (t % kSub == 0) ? f4_t{0.f, 0.f, 0.f, 0.f} : acc[m][j];
-          acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[m], B, c0, 0, 0, 0);
-        }
-        if (t % kSub == kSub - 1) {
-          const float sc = sb[p][j][u];
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) yacc[m][j][i] = fmaf(sc, acc[m][j][i], yacc[m][j][i]);
+      for (int i = 0; i < kChunks; ++i) {
+        bs[i] = b0;
+        cs[i] = c0;
+        b0 += db;
+        c0 += dc;
+        if (c0 >= cpr) {
+          c0 -= cpr;
+          ++b0;
         }
       }
-    }
-  };
+      u4_t stg[kChunks];
 #pragma unroll
-  for (int p = 0; p < NS; ++p)
-    if (p < ns) step(p);
+      for (int i = 0; i < kChunks; ++i) {
+        const int col = k0 * kStep + cs[i] * 8;
+        stg[i] = u4_t{0, 0, 0, 0};
+        if (bs[i] < a.batch && col < a.cols)
+          stg[i] = *reinterpret_cast<const u4_t *>(a.x + bs[i] * a.ldx + col);
+      }
+      // weights, scales and zeros of every step of the chunk, after x: loads
+      // complete in order, so x can be stored to LDS while the weights are
+      // still on their way (slots past the chunk repeat its last step: same
+      // cache lines, no branch, so the loads in flight are counted exactly)
+#pragma unroll
+      for (int p = 0; p < NS; ++p) issue(p, k0 + min(p, ns - 1));
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i)
+        if (bs[i] < 16 * MT) *reinterpret_cast<u4_t *>(xs + bs[i] * row_h + cs[i] * 8) = stg[i];
+    }
+    __syncthreads();
+
+    // One step: 4 MFMA sub-steps per slab and tile; the scale of each unit
+    // is applied to the unit's fp32 sum.
+    auto step = [&](const int p) {
+      const int s = p;
+      f4_t acc[MT][kNT];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        h8_t A[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          A[m] = *reinterpret_cast<const h8_t *>(xa + m * 16 * row_h + s * kStep + 32 * t);
+        const int u = t / kSub;
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) {
+          const uint32_t z = (zb[p][j][u] >> (4 * (n & 7))) & 15u;
+          const uint32_t nz1 = (0xE400u | z) * 0x00010001u;
+          const uint32_t nz2 = (0xD400u | (z << 4)) * 0x00010001u;
+          const h8_t B = dequant8(wb[p][j][t], nz1, nz2, dq);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const f4_t c0 = (t % kSub == 0) ? f4_t{0.f, 0.f, 0.f, 0.f} : acc[m][j];
+            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[m], B, c0, 0, 0, 0);
+          }
+          if (t % kSub == kSub - 1) {
+            const float sc = sb[p][j][u];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) yacc[m][j][i] = fmaf(sc, acc[m][j][i], yacc[m][j][i]);
+          }
+        }
+      }
+    };
+#pragma unroll
+    for (int p = 0; p < NS; ++p)
+      if (p < ns) step(p);
+  }
 
   // ---- output.  Lane holds C[m = 4 kg + i][n] of each 16 x 16 block.
   if (a.splits == 1) {
@@ -625,13 +634,14 @@ W4Plan plan_for(const Geometry &g, int bc, int cus) {
   W4Plan p;
   p.mt = (bc + 15) / 16;
   p.tiles = int(cdiv(g.rt16, kWaves * kNT));
-  const int ns_cap = std::min(kMaxNs, kStageChunks / p.mt);
-  const int s_min = int(cdiv(g.ksteps, ns_cap));
-  const int s_want = std::max(1, int(std::lround(2.0 * cus / p.tiles)));
-  p.splits = int(std::min<int64_t>(g.ksteps, std::max(s_min, s_want)));
+  const int ns_cap = std::min(kMaxNs, kStageChunks / p.mt);  // steps per staged chunk
+  // About two workgroups per CU, in one round: a split walks its steps in
+  // chunks of ns_cap, so the split count is free of the staging capacity
+  // (fewer splits, fewer partial sums written and read back).
+  p.splits = int(std::min<int64_t>(g.ksteps, std::max(1, 2 * cus / p.tiles)));
   p.base = int(g.ksteps / p.splits);
   p.rem = int(g.ksteps % p.splits);
-  p.ns_max = p.base + (p.rem ? 1 : 0);
+  p.ns_max = std::min(p.base + (p.rem ? 1 : 0), ns_cap);
   p.ns_t = p.ns_max <= 2 ? 2 : p.ns_max <= 4 ? 4 : 8;
   p.lds = size_t(16) * p.mt * (size_t(p.ns_max) * kStep + 8) * 2;
   return p;
