@@ -232,7 +232,9 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
     for (int t = 0; t < kPer; ++t) {
       const int e = min(tid + t * kSweepThreads, nq - 1);
       const int j = e / (B / 4), k = (e % (B / 4)) * 4;
-      v[t] = *reinterpret_cast<const f32x4_t *>(Ublk + int64_t(j) * ld + k);
+      // chunks wholly left of the diagonal are zero in LDS: not fetched
+      v[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (k + 3 >= j) v[t] = *reinterpret_cast<const f32x4_t *>(Ublk + int64_t(j) * ld + k);
     }
 #pragma unroll
     for (int t = 0; t < kPer; ++t) {
@@ -585,15 +587,22 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
         const float y = kQ4K ? (wj + M) * rS : wj * rs;
         const float r = __builtin_rintf(y);
         *tdist = fmaxf(*tdist, fabsf(y - r));
-        float qj, wq;
+        float qj, wq, ej;
         if (!kQ4K) {
-          qj = __builtin_amdgcn_fmed3f(r + z, 0.f, maxq);
-          wq = s * (qj - z);
+          // q - z = clamp(r, -z, maxq - z) (small integers: exact), and the
+          // division by U_jj is folded into both terms of w - s (q - z), so
+          // that a single fma follows the clamp on the column's dependent
+          // chain (one rounding of w / U_jj and of s / U_jj instead of one
+          // of w - s (q - z) and one of the quotient)
+          const float rq = __builtin_amdgcn_fmed3f(r, -z, maxq - z);
+          ej = fmaf(-(s * uinv), rq, wj * uinv);
+          qj = rq + z;
+          wq = s * rq;
         } else {
           qj = (S > 0.f) ? __builtin_amdgcn_fmed3f(r, 0.f, maxq) : 0.f;
           wq = S * qj - M;
+          ej = (wj - wq) * uinv;
         }
-        const float ej = (wj - wq) * uinv;
         // No masks: U's block row j is zero left of the diagonal (and past
         // B); a lane's finished columns are never read again.
 #pragma unroll
