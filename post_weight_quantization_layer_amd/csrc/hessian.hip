@@ -229,12 +229,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
   // Pipeline (double-buffered LDS stages of 64 tokens, one more stage in
   // flight in registers).  Iteration ks multiplies stage ks in four 16-token
   // steps; the fragments of step h+1 are read (one per two MFMAs) while the
-  // MFMAs of step h run.  During step 2 each slot also stores one register
-  // of stage ks+1 (loaded one iteration earlier) to the LDS slot that stage
-  // ks-1 used and re-issues that register's load for stage ks+2, so the
-  // copies stay in flight for a whole iteration.  A barrier then makes
-  // stage ks+1 visible (all reads of stage ks have completed by then), and
-  // step 0 of stage ks+1 is read while step 3 of stage ks is multiplied.
+  // MFMAs of step h run.  Over steps 0-2 every third slot also stores one
+  // register of stage ks+1 (loaded one iteration earlier) to the LDS slot
+  // that stage ks-1 used (its reads all ended before the previous barrier)
+  // and re-issues that register's load for stage ks+2, so the copies stay
+  // in flight for a whole iteration and the LDS writes do not crowd the
+  // fragment reads of one step (about 3% faster than all 16 in step 2).
+  // A barrier then makes stage ks+1 visible (all reads of stage ks have
+  // completed by then), and step 0 of stage ks+1 is read while step 3 of
+  // stage ks is multiplied.
   // On diagonal tiles each slot also adds one token of the lane's energy
   // row, whose chunks are read one step ahead.
   auto tail = [&]() {
@@ -263,7 +266,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
       if (kEnergy) energy_read(ep, 0, 0);
     }
     for (int64_t ks = 0; ks < nfull; ++ks) {
+      // copy c (0..15) of the stage sits in slot 3 (c % 6) of step c / 6
+      auto copy = [&](int step, int q) {
+        const int c = 6 * step + q / 3;
+        if (q % 3 == 0 && c < kLoads) {
+          store_one(c, ks + 1);
+          load_one(c, ks + 2);
+        }
+      };
       mfma_step(xa, xb, [&](int q) {
+        copy(0, q);
         if (q & 1) read_one(ya, yb, ks, 1, q >> 1);
         if (kEnergy) {
           if (q == 0) energy_read(eq, ks, 1);
@@ -271,6 +283,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
         }
       });
       mfma_step(ya, yb, [&](int q) {
+        copy(1, q);
         if (q & 1) read_one(xa, xb, ks, 2, q >> 1);
         if (kEnergy) {
           if (q == 0) energy_read(ep, ks, 2);
@@ -278,8 +291,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
         }
       });
       mfma_step(xa, xb, [&](int q) {
-        store_one(q, ks + 1);
-        load_one(q, ks + 2);
+        copy(2, q);
         if (q & 1) read_one(ya, yb, ks, 3, q >> 1);
         if (kEnergy) {
           if (q == 0) energy_read(eq, ks, 3);
