@@ -239,7 +239,7 @@ def main():
     ap.add_argument("--w4a16-iters", type=int, default=200)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(a layer's rows would shard across GPUs with one broadcast of U); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
