@@ -460,6 +460,25 @@ bool g_lds_set = false;
 bool g_rows_lds_set = false;
 constexpr size_t kMaxRowLds = 160 * 1024;
 
+// The same rotation four columns at a time (d a multiple of 4, 16-byte
+// aligned rows): the source of U[i][j..j+3] is the float4 of row d-1-i at
+// column d-4-j, reversed.  Chunks wholly below the diagonal are not read.
+__global__ void __launch_bounds__(256)
+    rotate_upper_vec_kernel(const float *__restrict__ Linv, int64_t d, float *__restrict__ U) {
+  const int64_t d4 = d / 4;
+  for (int64_t i = blockIdx.y; i < d; i += gridDim.y)
+    for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < d4; t += int64_t(gridDim.x) * 256) {
+      const int64_t j = 4 * t;
+      f32x4_t out = {0.f, 0.f, 0.f, 0.f};
+      if (j + 3 >= i) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(Linv + (d - 1 - i) * d + (d - 4 - j));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = j + e >= i ? v[3 - e] : 0.f;
+      }
+      *reinterpret_cast<f32x4_t *>(U + i * d + j) = out;
+    }
+}
+
 }  // namespace
 
 size_t prepare_ws_bytes(int64_t d) {
@@ -606,10 +625,17 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
     }
   }
 
-  GPTQ_TRY(launch("prep_rotate", rotate_upper_kernel,
-                  dim3((unsigned)std::min<int64_t>(cdiv(d, 256), 64), (unsigned)std::min<int64_t>(d, 16384)),
-                  dim3(256), 0,
-                  stream, (const float *)A, d, U));
+  if ((d & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(A) & 15) == 0)
+    GPTQ_TRY(launch("prep_rotate", rotate_upper_vec_kernel,
+                    dim3((unsigned)std::min<int64_t>(cdiv(d / 4, 256), 64),
+                         (unsigned)std::min<int64_t>(d, 16384)),
+                    dim3(256), 0, stream, (const float *)A, d, U));
+  else
+    GPTQ_TRY(launch("prep_rotate", rotate_upper_kernel,
+                    dim3((unsigned)std::min<int64_t>(cdiv(d, 256), 64), (unsigned)std::min<int64_t>(d, 16384)),
+                    dim3(256), 0,
+                    stream, (const float *)A, d, U));
 
   int host_flag = 0;
   hipError_t e = hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, stream);

@@ -711,6 +711,45 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// Form of the row-staged gather that also stages the column map in LDS,
+// once per workgroup, and walks rows grid-stride (about one workgroup per
+// CU): the map is read from memory once per workgroup instead of once per
+// row.  idx[p] is the source column of output position p, or -1 for a dead
+// column.  (The same staging made the scatter slower: with one workgroup
+// per CU its scattered LDS writes no longer overlap another row's loads.)
+__global__ void __launch_bounds__(256)
+    gather_cols_map_kernel(const float *__restrict__ W, int64_t rows, int64_t cols,
+                           const int32_t *__restrict__ perm, const uint8_t *__restrict__ dead,
+                           float *__restrict__ Wp) {
+  extern __shared__ float sm[];
+  float *srow = sm;
+  int32_t *idx = reinterpret_cast<int32_t *>(sm + cols);
+  for (int64_t p = threadIdx.x; p < cols; p += 256) {
+    const int32_t c = min(max(perm[p], 0), (int32_t)(cols - 1));
+    idx[p] = dead[c] ? -1 : c;
+  }
+  const bool vec = (cols & 3) == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    __syncthreads();  // the map is staged; the previous row's reads are done
+    const float *src = W + r * cols;
+    if (vec) {
+#pragma unroll 4
+      for (int64_t c4 = threadIdx.x; c4 < cols / 4; c4 += 256)
+        reinterpret_cast<f32x4_t *>(srow)[c4] = reinterpret_cast<const f32x4_t *>(src)[c4];
+    } else {
+#pragma unroll 4
+      for (int64_t c = threadIdx.x; c < cols; c += 256) srow[c] = src[c];
+    }
+    __syncthreads();
+    float *dst = Wp + r * cols;
+#pragma unroll 4
+    for (int64_t p = threadIdx.x; p < cols; p += 256) {
+      const int32_t c = idx[p];
+      dst[p] = c < 0 ? 0.f : srow[c];
+    }
+  }
+}
+
 // W[r][perm[p]] = Wp[r][p], q[r][perm[p]] = qp[r][p]
 __global__ void __launch_bounds__(256)
     scatter_cols_kernel(const float *__restrict__ Wp, const uint8_t *__restrict__ qp, int64_t rows,
@@ -781,12 +820,38 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   // wider rows take the plain kernels
   const size_t row_lds = size_t(cols) * 5;
   const unsigned growsn = (unsigned)std::min<int64_t>(rows, 65535);
+  // the map-staging gather: row and map in LDS (8 bytes per column)
+  constexpr size_t kMapLds = 160 * 1024;
+  const size_t map_lds = size_t(cols) * 8;
+  bool map_ok = false;
+  unsigned map_grid = 1;
+  if (p.act_order && map_lds <= kMapLds) {
+    static bool map_attr = false;
+    static int map_cus = 0;
+    if (!map_attr) {
+      int dev = 0, v = 0;
+      if (hipGetDevice(&dev) == hipSuccess &&
+          hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+        map_cus = v;
+      if (hipFuncSetAttribute((const void *)gather_cols_map_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMapLds) ==
+          hipSuccess)
+        map_attr = true;
+      else
+        map_cus = 0;
+    }
+    map_ok = map_attr && map_cus > 0;
+    map_grid = (unsigned)std::min<int64_t>(rows, std::max(map_cus, 1));
+  }
   if (p.act_order) {
     Wp = reinterpret_cast<float *>(base);
     base += align256(size_t(rows) * size_t(cols) * sizeof(float));
     qp = base;
     base += align256(size_t(rows) * size_t(cols));
-    if (row_lds <= 65536)
+    if (map_ok)
+      GPTQ_TRY(launch("quant_gather", gather_cols_map_kernel, dim3(map_grid), dim3(256), map_lds,
+                      stream, (const float *)W, rows, cols, perm, dead, Wp));
+    else if (row_lds <= 65536)
       GPTQ_TRY(launch("quant_gather", gather_cols_lds_kernel, dim3(growsn), dim3(256),
                       size_t(cols) * 4, stream, (const float *)W, rows, cols, perm, dead, Wp));
     else
