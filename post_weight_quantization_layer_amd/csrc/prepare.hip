@@ -165,6 +165,63 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// The same symmetrization launched over the upper tiles only (tile t of the
+// upper triangle, row-major), with float4 reads and writes (d a multiple of
+// 4, 16-byte aligned rows); tiles at the matrix edge take per-element masks.
+__global__ void __launch_bounds__(256)
+    symmetrize_vec_kernel(const float *__restrict__ H, int64_t d, int nt, float *__restrict__ S) {
+  // upper tile t -> (ti, tj), ti <= tj: row ti holds nt - ti tiles
+  int t = blockIdx.x, ti = 0;
+  while (t >= nt - ti) {
+    t -= nt - ti;
+    ++ti;
+  }
+  const int tj = ti + t;
+  __shared__ float tl[64][65];
+  const int64_t I0 = int64_t(ti) * 64, J0 = int64_t(tj) * 64;
+  const bool full = I0 + 64 <= d && J0 + 64 <= d;
+  const int c4 = (threadIdx.x & 15) * 4, r0 = threadIdx.x >> 4;  // 16 float4 per tile row
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = r0 + 16 * k;
+    const int64_t gr = I0 + r, gc = J0 + c4;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (full) {
+      const float4 x = *reinterpret_cast<const float4 *>(H + gr * d + gc);
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (gr < d && gc + e < d) ? H[gr * d + gc + e] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tl[r][c4 + e] = v[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = r0 + 16 * k;
+    float v[4], w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = c4 + e;
+      v[e] = (ti == tj && c < r) ? tl[c][r] : tl[r][c];  // tile (ti, tj)
+      w[e] = tl[c][r];                                     // tile (tj, ti), transposed
+    }
+    const int64_t gr = I0 + r, gc = J0 + c4;
+    const int64_t hr = J0 + r, hc = I0 + c4;
+    if (full) {
+      *reinterpret_cast<float4 *>(S + gr * d + gc) = make_float4(v[0], v[1], v[2], v[3]);
+      if (ti != tj) *reinterpret_cast<float4 *>(S + hr * d + hc) = make_float4(w[0], w[1], w[2], w[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (gr < d && gc + e < d) S[gr * d + gc + e] = v[e];
+        if (ti != tj && hr < d && hc + e < d) S[hr * d + hc + e] = w[e];
+      }
+    }
+  }
+}
+
 // Row a of A, on and below the diagonal: A[a][b] = Hp[d-1-a][d-1-b] with
 // Hp[x][y] = S[perm[x]][perm[y]] (S the symmetric H), dead diagonal entries
 // taken as 1 and delta added on the diagonal.  One workgroup per row: the
@@ -512,8 +569,13 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
                   stream, (const int32_t *)rank, d, (int)p.act_order, perm));
   // the symmetric H is staged in U's memory (U is written last)
   const unsigned g64 = (unsigned)cdiv(d, 64);
-  GPTQ_TRY(launch("prep_symmetrize", symmetrize_kernel, dim3(g64, g64), dim3(256), 0, stream, H, d,
-                  U));
+  if ((d & 3) == 0 && (reinterpret_cast<uintptr_t>(H) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(U) & 15) == 0)
+    GPTQ_TRY(launch("prep_symmetrize", symmetrize_vec_kernel, dim3(g64 * (g64 + 1) / 2), dim3(256),
+                    0, stream, H, d, (int)g64, U));
+  else
+    GPTQ_TRY(launch("prep_symmetrize", symmetrize_kernel, dim3(g64, g64), dim3(256), 0, stream, H,
+                    d, U));
   const unsigned growsn = (unsigned)std::min<int64_t>(d, 65535);
   const size_t srow_bytes = size_t(d) * sizeof(float);
   if (srow_bytes <= kMaxRowLds) {
