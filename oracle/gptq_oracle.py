@@ -151,12 +151,22 @@ def inverse_cholesky_upper_ul(Hp: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Grids.  Decisions in float32 (the kernel's precision), see module header.
 # --------------------------------------------------------------------------
-def affine_params(v: np.ndarray, bits: int):
+def _keep(name, pre, val):
+    """Default decision rule: the oracle's own rounding."""
+    return val
+
+
+def affine_params(v: np.ndarray, bits: int, decide=_keep):
     """Asymmetric min-max grid of one group for each row.
 
     v: (rows, g) current weights of the group.  The range always contains 0
     so that the zero point is an integer code in [0, maxq]; an all-zero group
-    uses the range [-1, 1].  Returns float32 (scale, zero, zero before rounding)."""
+    uses the range [-1, 1].  Returns float32 (scale, zero, zero before rounding).
+
+    ``decide(name, pre, val)`` returns the integer decision taken from the
+    pre-rounding value ``pre`` (here "zero"); the default keeps the oracle's
+    rounding ``val``.  Where ``pre`` sits on a tie, either rounding satisfies
+    the method, and a caller may adopt the other one."""
     maxq = f32(2 ** bits - 1)
     v = np.asarray(v, dtype=f32)
     xmin = np.minimum(v.min(axis=1), f32(0))
@@ -167,6 +177,7 @@ def affine_params(v: np.ndarray, bits: int):
     s = (xmax - xmin) / maxq
     zr = -xmin / s
     z = np.clip(np.rint(zr), f32(0), maxq)
+    z = decide("zero", zr, z)
     return s.astype(f32), z.astype(f32), zr.astype(f32)
 
 
@@ -181,7 +192,7 @@ def affine_params(v: np.ndarray, bits: int):
 SEARCH_SHRINK = np.array([1.0 - k / 32.0 for k in range(16)], dtype=f32)
 
 
-def affine_params_weighted(v: np.ndarray, h: np.ndarray, bits: int):
+def affine_params_weighted(v: np.ndarray, h: np.ndarray, bits: int, decide=_keep):
     """Affine grid of one group for each row by importance-weighted search.
 
     v: (rows, g) current weights of the group, h: (g,) importances.  For each
@@ -189,19 +200,23 @@ def affine_params_weighted(v: np.ndarray, h: np.ndarray, bits: int):
     q = clamp(rint(v / s_k) + z0, 0, maxq) and w^ = s_k (q - z0) in float32,
     E_k = sum_i h_i (v_i - w^_i)^2 in float64.  Returns float32 (scale, zero,
     zero before rounding) and, for each row, the relative gap between the
-    least and the next-least E_k (0 when the choice is a tie)."""
-    s0, z0, zr = affine_params(v, bits)
+    least and the next-least E_k (0 when the choice is a tie).  ``decide`` as
+    in affine_params ("zero", then "search" with pre = (E, candidate scales))."""
+    s0, z0, zr = affine_params(v, bits, decide)
     maxq = f32(2 ** bits - 1)
     v = np.asarray(v, dtype=f32)
     h = np.asarray(h, dtype=np.float64)
     E = np.empty((len(SEARCH_SHRINK), v.shape[0]))
+    cand = np.empty((len(SEARCH_SHRINK), v.shape[0]), f32)
     for k, f in enumerate(SEARCH_SHRINK):
         s = (f * s0).astype(f32)
+        cand[k] = s
         q = np.clip(np.rint(v / s[:, None]) + z0[:, None], f32(0), maxq)
         what = (s[:, None] * (q - z0[:, None])).astype(f32)
         d = (v - what).astype(np.float64)
         E[k] = (h[None, :] * (d * d)).sum(axis=1)
     best = np.argmin(E, axis=0)                    # first least error
+    best = decide("search", (E, cand), best)
     s = (SEARCH_SHRINK[best] * s0).astype(f32)
     Es = np.sort(E, axis=0)
     with np.errstate(divide="ignore", invalid="ignore"):
@@ -209,11 +224,14 @@ def affine_params_weighted(v: np.ndarray, h: np.ndarray, bits: int):
     return s, z0, zr, gap
 
 
-def affine_quantize(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int):
-    """Code and dequantized value of one column: q = clamp(rint(w/s)+z), w^ = s(q-z)."""
+def affine_quantize(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int, decide=_keep):
+    """Code and dequantized value of one column: q = clamp(rint(w/s)+z), w^ = s(q-z).
+    ``decide`` as in affine_params ("code", pre = w/s)."""
     maxq = f32(2 ** bits - 1)
     w = np.asarray(w, dtype=f32)
-    q = np.clip(np.rint(w / s) + z, f32(0), maxq)
+    ratio = w / s
+    q = np.clip(np.rint(ratio) + z, f32(0), maxq)
+    q = decide("code", ratio, q)
     return q.astype(f32), (s * (q - z)).astype(f32)
 
 
@@ -232,7 +250,7 @@ def kquant_sub_bits(bits: int) -> int:
     return widths[bits]
 
 
-def q4k_params(v: np.ndarray, bits: int = 4):
+def q4k_params(v: np.ndarray, bits: int = 4, decide=_keep):
     """Two-level grid of one super-block of 256 weights for each row.
 
     From "Add gguf q4_k quantization": w = q * block_scale + block_min with
@@ -249,9 +267,10 @@ def q4k_params(v: np.ndarray, bits: int = 4):
     mc_b = clamp(rint(m_b / Dm), 0, kmax) if Dm > 0 else 0;
     effective S_b = D sc_b, M_b = Dm mc_b.
 
-    Returns D, Dm (float16), sc, mc (uint8, (rows, 8)), S, M (float32, (rows, 8))."""
+    Returns D, Dm (float16), sc, mc (uint8, (rows, 8)), S, M (float32, (rows, 8)).
+    ``decide`` as in affine_params, for "D" and "Dm" (pre: the float32 value
+    rounded to fp16) and then "sc" and "mc" (pre: s_b/D and m_b/Dm)."""
     maxq = f32(2 ** bits - 1)
-    kmax = f32(2 ** kquant_sub_bits(bits) - 1)
     v = np.asarray(v, dtype=f32)
     rows = v.shape[0]
     vb = v.reshape(rows, Q4K_SUPER // Q4K_SUB, Q4K_SUB)
@@ -259,21 +278,32 @@ def q4k_params(v: np.ndarray, bits: int = 4):
     mx = np.maximum(vb.max(axis=2), f32(0))
     s_b = (mx - mn) / maxq
     m_b = -mn
-    D = (s_b.max(axis=1) / kmax).astype(np.float16)
-    Dm = (m_b.max(axis=1) / kmax).astype(np.float16)
+    return _q4k_second_level(s_b, m_b, bits, decide)
+
+
+def _q4k_second_level(s_b, m_b, bits, decide):
+    """Super-block level of the two-level grid from the sub-block (scale, min)
+    pairs s_b, m_b (rows, 8): fp16 D and Dm, then the sub-block codes."""
+    kmax = f32(2 ** kquant_sub_bits(bits) - 1)
+    xd = s_b.max(axis=1) / kmax
+    xm = m_b.max(axis=1) / kmax
+    D = decide("D", xd, xd.astype(np.float16))
+    Dm = decide("Dm", xm, xm.astype(np.float16))
     Df = D.astype(f32)[:, None]
     Dmf = Dm.astype(f32)[:, None]
     with np.errstate(divide="ignore", invalid="ignore"):
-        sc = np.where((s_b > 0) & (Df > 0), np.clip(np.rint(s_b / Df), 1, kmax), 0)
-        mc = np.where(Dmf > 0, np.clip(np.rint(m_b / Dmf), 0, kmax), 0)
-    sc = sc.astype(f32)
-    mc = mc.astype(f32)
+        rs = s_b / Df
+        rm = m_b / Dmf
+        sc = np.where((s_b > 0) & (Df > 0), np.clip(np.rint(rs), 1, kmax), 0)
+        mc = np.where(Dmf > 0, np.clip(np.rint(rm), 0, kmax), 0)
+    sc = decide("sc", rs, sc.astype(f32))
+    mc = decide("mc", rm, mc.astype(f32))
     S = (Df * sc).astype(f32)
     M = (Dmf * mc).astype(f32)
     return D, Dm, sc.astype(np.uint8), mc.astype(np.uint8), S, M
 
 
-def q4k_params_weighted(v: np.ndarray, h: np.ndarray, bits: int = 4):
+def q4k_params_weighted(v: np.ndarray, h: np.ndarray, bits: int = 4, decide=_keep):
     """Two-level grid of one super-block for each row by importance-weighted
     search of each sub-block's scale and min, then the same second level as
     q4k_params.
@@ -285,9 +315,9 @@ def q4k_params_weighted(v: np.ndarray, h: np.ndarray, bits: int = 4):
     E_k = sum_i h_i (v_i - w^_i)^2 in float64; the first least E_k gives the
     sub-block's (s_b, m_b), from which D, Dm, sc, mc follow as in q4k_params.
     Returns those six arrays and the relative gap of each sub-block's choice
-    (rows, 8)."""
+    (rows, 8).  ``decide`` as in q4k_params, with first "search" (pre = (E,
+    candidate scales, candidate mins), each (16, rows, 8))."""
     maxq = f32(2 ** bits - 1)
-    kmax = f32(2 ** kquant_sub_bits(bits) - 1)
     v = np.asarray(v, dtype=f32)
     h = np.asarray(h, dtype=np.float64)
     rows = v.shape[0]
@@ -299,9 +329,12 @@ def q4k_params_weighted(v: np.ndarray, h: np.ndarray, bits: int = 4):
     s0 = (mx - mn) / maxq
     m0 = -mn
     E = np.empty((len(SEARCH_SHRINK), rows, nb))
+    cs = np.empty((len(SEARCH_SHRINK), rows, nb), f32)
+    cm = np.empty((len(SEARCH_SHRINK), rows, nb), f32)
     for k, f in enumerate(SEARCH_SHRINK):
         s = (f * s0).astype(f32)
         m = (f * m0).astype(f32)
+        cs[k], cm[k] = s, m
         with np.errstate(divide="ignore", invalid="ignore"):
             q = np.where(s[..., None] > 0,
                          np.clip(np.rint((vb + m[..., None]) / s[..., None]), f32(0), maxq),
@@ -310,31 +343,25 @@ def q4k_params_weighted(v: np.ndarray, h: np.ndarray, bits: int = 4):
         d = (vb - what).astype(np.float64)
         E[k] = (hb[None, :, :] * (d * d)).sum(axis=2)
     best = np.argmin(E, axis=0)
+    best = decide("search", (E, cs, cm), best)
     s_b = (SEARCH_SHRINK[best] * s0).astype(f32)
     m_b = (SEARCH_SHRINK[best] * m0).astype(f32)
     Es = np.sort(E, axis=0)
     with np.errstate(divide="ignore", invalid="ignore"):
         gap = np.where(Es[0] > 0, (Es[1] - Es[0]) / Es[0], np.where(Es[1] > 0, np.inf, 0.0))
-    D = (s_b.max(axis=1) / kmax).astype(np.float16)
-    Dm = (m_b.max(axis=1) / kmax).astype(np.float16)
-    Df = D.astype(f32)[:, None]
-    Dmf = Dm.astype(f32)[:, None]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        sc = np.where((s_b > 0) & (Df > 0), np.clip(np.rint(s_b / Df), 1, kmax), 0)
-        mc = np.where(Dmf > 0, np.clip(np.rint(m_b / Dmf), 0, kmax), 0)
-    sc = sc.astype(f32)
-    mc = mc.astype(f32)
-    S = (Df * sc).astype(f32)
-    M = (Dmf * mc).astype(f32)
-    return D, Dm, sc.astype(np.uint8), mc.astype(np.uint8), S, M, s_b, m_b, gap
+    D, Dm, sc, mc, S, M = _q4k_second_level(s_b, m_b, bits, decide)
+    return D, Dm, sc, mc, S, M, s_b, m_b, gap
 
 
-def q4k_quantize(w: np.ndarray, S: np.ndarray, M: np.ndarray, bits: int = 4):
-    """q = clamp(rint((w + M)/S), 0, 2^bits - 1) (0 when S = 0), w^ = S q - M."""
+def q4k_quantize(w: np.ndarray, S: np.ndarray, M: np.ndarray, bits: int = 4, decide=_keep):
+    """q = clamp(rint((w + M)/S), 0, 2^bits - 1) (0 when S = 0), w^ = S q - M.
+    ``decide`` as in affine_params ("code", pre = (w + M)/S)."""
     w = np.asarray(w, dtype=f32)
     maxq = f32(2 ** bits - 1)
     with np.errstate(divide="ignore", invalid="ignore"):
-        q = np.where(S > 0, np.clip(np.rint((w + M) / S), 0, maxq), 0).astype(f32)
+        ratio = (w + M) / S
+        q = np.where(S > 0, np.clip(np.rint(ratio), 0, maxq), 0).astype(f32)
+    q = decide("code", ratio, q)
     return q, (S * q - M).astype(f32)
 
 
@@ -371,11 +398,16 @@ class SweepResult:
 
 
 class _GroupState:
-    """Grid parameters of the group (super-block) currently being quantized."""
+    """Grid parameters of the group (super-block) currently being quantized.
 
-    def __init__(self, spec: GridSpec, rows: int, d: int, importance=None):
+    ``decide(name, j, pre, val)``, when given, is consulted for every integer
+    or fp16 decision taken at column j (see affine_params); None keeps the
+    oracle's own rounding everywhere."""
+
+    def __init__(self, spec: GridSpec, rows: int, d: int, importance=None, decide=None):
         self.spec = spec
         self.importance = importance
+        self.decide = decide
         ng = d // spec.span
         self.sgap = np.full((rows, ng), np.inf)
         if spec.grid == "affine":
@@ -395,27 +427,33 @@ class _GroupState:
             self.mc = np.zeros((rows, nsub), np.uint8)
             self.subgap = np.full((rows, nsub), np.inf)
 
+    def _at(self, j: int):
+        if self.decide is None:
+            return _keep
+        return lambda name, pre, val: self.decide(name, j, pre, val)
+
     def choose(self, j: int, v: np.ndarray):
         """Choose the grid of the group starting at column j from current weights v."""
         sp = self.spec
         gi = j // sp.span
+        dec = self._at(j)
         if sp.grid == "affine" and sp.search:
             h = self.importance[j:j + v.shape[1]]
-            s, z, zr, gap = affine_params_weighted(v, h, sp.bits)
+            s, z, zr, gap = affine_params_weighted(v, h, sp.bits, dec)
             self.scale[:, gi], self.zero[:, gi], self.zratio[:, gi] = s, z, zr
             self.sgap[:, gi] = gap
         elif sp.grid == "affine":
-            s, z, zr = affine_params(v, sp.bits)
+            s, z, zr = affine_params(v, sp.bits, dec)
             self.scale[:, gi], self.zero[:, gi], self.zratio[:, gi] = s, z, zr
         else:
             b0 = j // Q4K_SUB
             nb = Q4K_SUPER // Q4K_SUB
             if sp.search:
                 h = self.importance[j:j + v.shape[1]]
-                D, Dm, sc, mc, S, M, s_b, m_b, gap = q4k_params_weighted(v, h, sp.bits)
+                D, Dm, sc, mc, S, M, s_b, m_b, gap = q4k_params_weighted(v, h, sp.bits, dec)
                 self.subgap[:, b0:b0 + nb] = gap
             else:
-                D, Dm, sc, mc, S, M = q4k_params(v, sp.bits)
+                D, Dm, sc, mc, S, M = q4k_params(v, sp.bits, dec)
                 vb = np.asarray(v, f32).reshape(v.shape[0], nb, Q4K_SUB)
                 mn = np.minimum(vb.min(axis=2), f32(0))
                 mx = np.maximum(vb.max(axis=2), f32(0))
@@ -433,12 +471,12 @@ class _GroupState:
         if sp.grid == "affine":
             gi = j // sp.group
             s, z = self.scale[:, gi], self.zero[:, gi]
-            q, what = affine_quantize(w, s, z, sp.bits)
+            q, what = affine_quantize(w, s, z, sp.bits, self._at(j))
             ratio = np.asarray(w, f32) / s
         else:
             b = j // Q4K_SUB
             S, M = self.scale[:, b], self.zero[:, b]
-            q, what = q4k_quantize(w, S, M, sp.bits)
+            q, what = q4k_quantize(w, S, M, sp.bits, self._at(j))
             with np.errstate(divide="ignore", invalid="ignore"):
                 ratio = (np.asarray(w, f32) + M) / S
         return q, what, ratio
@@ -455,14 +493,18 @@ def _check_shapes(W, U, spec: GridSpec, block: int | None):
 
 
 def gptq_sweep(Wp: np.ndarray, U: np.ndarray, spec: GridSpec,
-               block: int | None = None, importance=None) -> SweepResult:
+               block: int | None = None, importance=None, decide=None) -> SweepResult:
     """Quantize Wp (rows x d, processing order) column by column.
 
     block=None is the plain definition: after column j every later column k
     takes W[:, k] -= e_j U[j, k] at once, with e_j = (w_j - w^_j)/U[j, j].
     block=B is the lazy blocked form: inside a block of B columns the update
     reaches only the block's own later columns, and the accumulated errors
-    reach everything after the block in one product Err @ U[block, after]."""
+    reach everything after the block in one product Err @ U[block, after].
+
+    ``decide(name, j, pre, val)`` may replace a rounding decision taken on a
+    tie by the other, equally valid one (see affine_params); None keeps the
+    oracle's own."""
     _check_shapes(Wp, U, spec, block)
     W = np.array(Wp, dtype=np.float64)
     U = np.asarray(U, dtype=np.float64)
@@ -472,7 +514,7 @@ def gptq_sweep(Wp: np.ndarray, U: np.ndarray, spec: GridSpec,
     ratio = np.zeros((r, d), f32)
     if spec.search and importance is None:
         raise ValueError("the weighted grid search needs the columns' importances")
-    gs = _GroupState(spec, r, d, importance)
+    gs = _GroupState(spec, r, d, importance, decide)
     B = d if block is None else block
     for i1 in range(0, d, B):
         i2 = min(i1 + B, d)

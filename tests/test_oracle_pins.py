@@ -644,6 +644,36 @@ def test_q4k_weighted_search_between_minmax_and_optimum(bits):
     assert improved > 0
 
 
+def test_q4k_weighted_search_ignores_unimportant_outliers():
+    """One sub-block on the grid (s, m) = (22/32) x its min-max pair, plus two
+    outliers of importance 0 that alone set that pair: the search lands on
+    candidate k = 10 exactly, with zero weighted error; with all importances 1
+    it does not.  All values are exact in float32 (s0 = 2^-5, m0 = 96 2^-12)."""
+    bits, maxq = 4, 15
+    s0, m0 = np.float32(2.0 ** -5), np.float32(96 * 2.0 ** -12)
+    t = np.float32(22 * 2.0 ** -10)           # (22/32) s0
+    m = np.float32(66 * 2.0 ** -12)           # (22/32) m0
+    assert t == np.float32(O.SEARCH_SHRINK[10] * s0) and m == np.float32(O.SEARCH_SHRINK[10] * m0)
+    codes = np.array([0, 1, 2, 3, 5, 6, 8, 9, 10, 11, 12, 13, 14, 15, 7, 4] * 2)[:30]
+    sub = np.concatenate([(t * codes - m).astype(np.float32),
+                          np.array([-m0, -m0 + maxq * s0], np.float32)])
+    v = np.zeros((1, 256), np.float32)
+    v[0, 64:96] = sub                          # sub-block 2; the others are all zero
+    h = np.ones(256)
+    h[94:96] = 0.0
+    out = O.q4k_params_weighted(v, h, bits)
+    s_b, m_b = out[6], out[7]
+    assert s_b[0, 2] == t and m_b[0, 2] == m
+    assert _q4k_sub_error(sub, h[64:96], t, m, bits) == 0.0
+    # the min-max pair itself is what the sub-block's extremes give
+    mn, mx = min(sub.min(), 0), max(sub.max(), 0)
+    assert np.float32(np.float32(mx - mn) / np.float32(maxq)) == s0 and -mn == m0
+    # zero sub-blocks: every candidate is exact, the first (k = 0) is kept
+    assert np.all(s_b[0, [0, 1, 3, 4, 5, 6, 7]] == 0)
+    out1 = O.q4k_params_weighted(v, np.ones(256), bits)
+    assert not (out1[6][0, 2] == t and out1[7][0, 2] == m)
+
+
 def test_q4k_weighted_search_layer_invariants():
     rng = np.random.default_rng(90)
     W, X = rand_layer(rng, 12, 512, 900, outliers=4)
