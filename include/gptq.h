@@ -31,8 +31,11 @@
  *    unless a leading dimension is given.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = legacy default
  *    stream) and is asynchronous, except where stated.  The library keeps no
- *    device state between calls; calls on different streams may run
- *    concurrently as long as their buffers are distinct.
+ *    device state between calls; calls on different streams, from one or
+ *    several host threads, may run concurrently as long as their buffers are
+ *    distinct.  Its only host state is a lock-guarded cache of per-device
+ *    attributes (kernel LDS limits, compute-unit count), the thread-local
+ *    error text and the profiler (which is single-threaded).
  *  - The library never allocates device memory.  Scratch memory is the
  *    caller's `ws` buffer of `ws_bytes` bytes, sized by
  *    gptq_workspace_bytes() and 256-byte aligned.

@@ -3,7 +3,9 @@
 #include <cmath>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "common.h"
@@ -96,6 +98,40 @@ void profile_end(ProfileToken tok, hipStream_t stream) {
   (void)hipEventRecord(stop, stream);
   P.pending.push_back({tok.slot, tok.start, stop});
   if (P.pending.size() > (size_t(1) << 18)) P.drain();
+}
+
+// ------------------------------------------------------- per-device set-up
+namespace {
+std::mutex g_setup_mu;
+std::map<std::pair<const void *, int>, size_t> g_lds_limit;  // (kernel, device) -> bytes
+std::map<int, int> g_cu_count;                               // device -> compute units
+}  // namespace
+
+gptq_status allow_dynamic_lds(const void *kernel, size_t bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(GPTQ_ERR_DEVICE, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(g_setup_mu);
+  auto key = std::make_pair(kernel, dev);
+  auto it = g_lds_limit.find(key);
+  if (it != g_lds_limit.end() && it->second >= bytes) return GPTQ_OK;
+  hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess)
+    return fail(GPTQ_ERR_DEVICE, std::string("cannot raise LDS limit: ") + hipGetErrorString(e));
+  g_lds_limit[key] = bytes;
+  return GPTQ_OK;
+}
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(g_setup_mu);
+  auto it = g_cu_count.find(dev);
+  if (it != g_cu_count.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  g_cu_count[dev] = n;
+  return n;
 }
 
 // ------------------------------------------------------------- validation

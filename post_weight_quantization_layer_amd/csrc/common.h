@@ -38,6 +38,13 @@ inline gptq_status launch(const char *name, Kernel kernel, dim3 grid, dim3 block
   return GPTQ_OK;
 }
 
+// Per-device set-up shared by all entry points, safe to call from several
+// host threads at once (a lock guards the caches): raise a kernel's dynamic
+// LDS limit on the current device (once per kernel, device and size), and
+// the current device's compute-unit count (256 if it cannot be read).
+gptq_status allow_dynamic_lds(const void *kernel, size_t bytes);
+int device_cu_count();
+
 #define GPTQ_TRY(expr)                  \
   do {                                  \
     gptq_status _st = (expr);           \

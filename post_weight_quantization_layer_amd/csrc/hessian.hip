@@ -436,14 +436,7 @@ gptq_status hessian_accumulate_impl(float *H, double *hdiag, int64_t d, const vo
     const int ntiles = nt * (nt + 1) / 2;
     const int per_xcd = (int)cdiv(ntiles, 8);
     const size_t lds = size_t(kStages) * kStageBytes;
-    static bool lds_set = false;
-    if (!lds_set) {
-      hipError_t e = hipFuncSetAttribute((const void *)syrk_bf16_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess)
-        return fail(GPTQ_ERR_DEVICE, std::string("cannot raise LDS limit: ") + hipGetErrorString(e));
-      lds_set = true;
-    }
+    GPTQ_TRY(allow_dynamic_lds((const void *)syrk_bf16_kernel, lds));
     GPTQ_TRY(launch("hessian_syrk_bf16", syrk_bf16_kernel, dim3(8 * per_xcd), dim3(kThreads), lds,
                     stream, H, hdiag, Xb, d, n_tok, ld_x, nt, ntiles, per_xcd));
   } else {

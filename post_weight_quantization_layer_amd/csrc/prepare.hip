@@ -513,8 +513,6 @@ __global__ void __launch_bounds__(256)
       U[i * d + j] = j >= i ? Linv[(d - 1 - i) * d + (d - 1 - j)] : 0.f;
 }
 
-bool g_lds_set = false;
-bool g_rows_lds_set = false;
 constexpr size_t kMaxRowLds = 160 * 1024;
 
 // The same rotation four columns at a time (d a multiple of 4, 16-byte
@@ -579,14 +577,8 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
   const unsigned growsn = (unsigned)std::min<int64_t>(d, 65535);
   const size_t srow_bytes = size_t(d) * sizeof(float);
   if (srow_bytes <= kMaxRowLds) {
-    if (srow_bytes > 65536 && !g_rows_lds_set) {
-      hipError_t e = hipFuncSetAttribute((const void *)gather_rows_kernel<true>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)kMaxRowLds);
-      if (e != hipSuccess)
-        return fail(GPTQ_ERR_DEVICE, std::string("cannot raise LDS limit: ") + hipGetErrorString(e));
-      g_rows_lds_set = true;
-    }
+    if (srow_bytes > 65536)
+      GPTQ_TRY(allow_dynamic_lds((const void *)gather_rows_kernel<true>, kMaxRowLds));
     GPTQ_TRY(launch("prep_gather", gather_rows_kernel<true>, dim3(growsn), dim3(256), srow_bytes,
                     stream, (const float *)U, d, (const int32_t *)perm, (const uint8_t *)dead,
                     (const double *)delta, A));
@@ -598,13 +590,7 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
 
   // ---- blocked Cholesky A = L L^T; diagonal blocks end up holding L_ii^-1
   const size_t lds = kDiagLds;
-  if (!g_lds_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)potrf_inv_block_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess)
-      return fail(GPTQ_ERR_DEVICE, std::string("cannot raise LDS limit: ") + hipGetErrorString(e));
-    g_lds_set = true;
-  }
+  GPTQ_TRY(allow_dynamic_lds((const void *)potrf_inv_block_kernel, lds));
   // Two levels: the trailing update inside a panel of kPanel columns is
   // applied after each diagonal block (K = 128), the update of the columns
   // past the panel once per panel (K = kPanel).

@@ -93,17 +93,24 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// Half-width of the window around a half-integer inside which y = num * rden
+// (rden = 1/den rounded) and the IEEE quotient num / den may round to
+// different integers.  rden and the product each carry a relative error of
+// at most 2^-24, and the IEEE quotient one more, so the two differ by at most
+// |y| * 3 * 2^-24 < |y| * 1.8e-7; the window is 1e-5 + |y| * 2.5e-7.  With the
+// zero point the quotient reaches |num/den| = 2^bits - 1 (255 at 8 bits,
+// where the relative term is 6.4e-5).
+__device__ __forceinline__ float tie_window(float y) { return fmaf(fabsf(y), 2.5e-7f, 1e-5f); }
+
 // rint(num / den) exactly as if num / den were computed with a correctly
-// rounded IEEE division: the quotient is formed as num * rden (rden ~ 1/den)
-// and only when that lands within 1e-5 of a half-integer -- where the two
-// roundings could disagree -- is the IEEE division done.  |num/den| <= 32 is
-// all that matters here (larger values are clamped away); there the product
-// is within 3 ulp (< 6e-6) of the IEEE quotient.  The exact path is a
+// rounded IEEE division: the quotient is formed as num * rden and only when
+// that lands inside tie_window of a half-integer -- where the two roundings
+// could disagree -- is the IEEE division done.  The exact path is a
 // wavefront-uniform branch taken only when some lane is near a tie.
 __device__ __forceinline__ float rint_div(float num, float den, float rden) {
   const float y = num * rden;
   float r = __builtin_rintf(y);
-  const bool near = fabsf(y - floorf(y) - 0.5f) < 1e-5f;
+  const bool near = fabsf(y - floorf(y) - 0.5f) < tie_window(y);
   if (__builtin_expect(__any(near), 0)) r = near ? __builtin_rintf(num / den) : r;
   return r;
 }
@@ -149,14 +156,6 @@ template <int kSub>
 __device__ __forceinline__ float row_bcast(float v) {
   return __int_as_float(
       __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + kSub, 0xf, 0xf, false));
-}
-
-// rint(y) where y = num * (1/den) approximates num / den; *tie is set when y
-// lies within 1e-5 of a half-integer, where the exact quotient could round
-// the other way (see rint_div).
-__device__ __forceinline__ float rint_fast(float y, bool *tie) {
-  *tie |= fabsf(y - floorf(y) - 0.5f) < 1e-5f;
-  return __builtin_rintf(y);
 }
 
 template <int I, int N, typename F>
@@ -558,9 +557,10 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
     float pbi = Uinv[1];
     // Fast pass over one 8-column step whose owner (lane j8/8 of each row)
     // is the immediate kOwner, so that w_j is broadcast with one DPP move.
-    // It rounds w_j * (1/s) directly and tracks the largest distance of a
-    // rounded value from its integer: past 0.5 - 1e-5 the exact quotient
-    // could round the other way.
+    // It rounds w_j * (1/s) directly and tracks, for every rounded value,
+    // its distance from its integer plus the value-dependent part of
+    // tie_window: past 0.5 - 1e-5 the exact quotient could round the other
+    // way.
     auto fast_step = [&](auto owner, float *tdist) {
       constexpr int kOwner = decltype(owner)::value;
       constexpr int j8 = kOwner * kCPL;
@@ -586,7 +586,7 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
         const float wj = row_bcast<kOwner>(w[x]);
         const float y = kQ4K ? (wj + M) * rS : wj * rs;
         const float r = __builtin_rintf(y);
-        *tdist = fmaxf(*tdist, fabsf(y - r));
+        *tdist = fmaxf(*tdist, fmaf(fabsf(y), 2.5e-7f, fabsf(y - r)));
         float qj, wq, ej;
         if (!kQ4K) {
           // q - z = clamp(r, -z, maxq - z) (small integers: exact), and the
@@ -788,8 +788,6 @@ __global__ void __launch_bounds__(256)
   if (j < cols) hp[j] = hdiag[perm[j]];
 }
 
-bool g_sweep_lds_set[4] = {false, false, false, false};
-
 }  // namespace
 
 size_t quantize_ws_bytes(int64_t rows, int64_t cols, const gptq_params &p) {
@@ -826,21 +824,10 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   bool map_ok = false;
   unsigned map_grid = 1;
   if (p.act_order && map_lds <= kMapLds) {
-    static bool map_attr = false;
-    static int map_cus = 0;
-    if (!map_attr) {
-      int dev = 0, v = 0;
-      if (hipGetDevice(&dev) == hipSuccess &&
-          hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-        map_cus = v;
-      if (hipFuncSetAttribute((const void *)gather_cols_map_kernel,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMapLds) ==
-          hipSuccess)
-        map_attr = true;
-      else
-        map_cus = 0;
-    }
-    map_ok = map_attr && map_cus > 0;
+    // without the larger LDS limit the row-staged gather below serves
+    map_ok = allow_dynamic_lds((const void *)gather_cols_map_kernel, kMapLds) == GPTQ_OK;
+    if (!map_ok) set_error("");
+    const int map_cus = device_cu_count();
     map_grid = (unsigned)std::min<int64_t>(rows, std::max(map_cus, 1));
   }
   if (p.act_order) {
@@ -886,22 +873,8 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   // has a SIMD to itself: the sweep is a chain of dependent steps per row,
   // and a second wavefront on the SIMD would only halve its issue rate.
   constexpr size_t kSoloLds = 96 * 1024;
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-      n_cu = v;
-    else
-      n_cu = -1;
-  }
-  if (!g_sweep_lds_set[variant]) {
-    hipError_t e = hipFuncSetAttribute(kfn[variant], hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)std::max(lds, kSoloLds));
-    if (e != hipSuccess)
-      return fail(GPTQ_ERR_DEVICE, std::string("cannot raise LDS limit: ") + hipGetErrorString(e));
-    g_sweep_lds_set[variant] = true;
-  }
+  const int n_cu = device_cu_count();
+  GPTQ_TRY(allow_dynamic_lds(kfn[variant], std::max(lds, kSoloLds)));
   const unsigned nwg = (unsigned)std::min<int64_t>(cdiv(rows, kSweepThreads / 64 * 4), kSweepMaxWG);
   const size_t lds_launch = (n_cu > 0 && nwg <= (unsigned)n_cu) ? std::max(lds, kSoloLds) : lds;
 

@@ -578,19 +578,7 @@ __global__ __launch_bounds__(NSW > 8 ? 512 : 1024) void w4a16_rows_kernel(W4Args
 }
 
 // ------------------------------------------------------------ launch plan
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
+int cu_count() { return device_cu_count(); }
 
 constexpr size_t kRowsLdsMax = 144 * 1024;   // LDS of the rows kernel, at most
 constexpr int kRowsMaxBatch = 16;
@@ -662,22 +650,10 @@ size_t ws_bytes_for(const Geometry &g, bool permuted, int64_t batch, int cus) {
   return xp + part;
 }
 
-template <typename K>
-gptq_status allow_lds(K kern, size_t bytes, bool &done) {
-  if (!done) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes)) != hipSuccess)
-      return fail(GPTQ_ERR_DEVICE, "hipFuncSetAttribute failed for a w4a16 kernel");
-    done = true;
-  }
-  return GPTQ_OK;
-}
-
 template <int MT, int SPS, int NS>
 gptq_status launch_gemm(const W4Args &a, const W4Plan &p, hipStream_t stream) {
-  static bool attr_set = false;
   auto kern = w4a16_gemm_kernel<MT, SPS, NS>;
-  GPTQ_TRY(allow_lds(kern, 96 * 1024, attr_set));
+  GPTQ_TRY(allow_dynamic_lds(reinterpret_cast<const void *>(kern), 96 * 1024));
   return launch("w4a16_gemm", kern, dim3(p.tiles * p.splits), dim3(kThreads), p.lds, stream, a);
 }
 
@@ -701,9 +677,8 @@ gptq_status launch_gemm_sps(const W4Args &a, const W4Plan &p, int sps, hipStream
 
 template <int SPS, int NSW>
 gptq_status launch_rows(const W4Args &a, const RowsPlan &r, hipStream_t stream) {
-  static bool attr_set = false;
   auto kern = w4a16_rows_kernel<SPS, NSW>;
-  GPTQ_TRY(allow_lds(kern, kRowsLdsMax, attr_set));
+  GPTQ_TRY(allow_dynamic_lds(reinterpret_cast<const void *>(kern), kRowsLdsMax));
   return launch("w4a16_gemm", kern, dim3(a.rt16), dim3(64 * r.waves), r.lds, stream, a);
 }
 
