@@ -93,3 +93,26 @@ def oracle_layer(cfg: I.LayerConfig, W: np.ndarray, chunks_f32, block=None, sear
                            act_order=cfg.act_order, percdamp=cfg.percdamp, grid=cfg.grid,
                            search=search)
     return res, H, diag
+
+
+def gpu_grid(g: GpuOut, grid: str) -> dict:
+    """The GPU's grid outputs (processing order) in the form the tie-forced
+    replay compares."""
+    if grid == "affine":
+        return {"scale": g.scale, "zero": g.zero}
+    return {"D": g.D, "Dm": g.Dm, "sc": g.sc, "mc": g.mc}
+
+
+def check_replay(cfg: I.LayerConfig, W: np.ndarray, o, g: GpuOut, diag=None, search=False,
+                 max_frac: float = 1e-3, max_search_rows=None, tag: str = ""):
+    """Tie-forced replay of the oracle's sweep against the GPU's decisions,
+    asserted (see tests.parity.assert_replay); returns the report."""
+    from tests.parity import assert_replay, replay_layer
+    grid = gpu_grid(g, cfg.grid)
+    rp = replay_layer(W, o, g.q, grid, grid_kind=cfg.grid, bits=cfg.bits, group=cfg.group,
+                      diag=diag, search=search)
+    log(f"[replay] {tag}: adopted {rp.forced} at ties ({rp.search_ties} search-tie "
+        f"super-blocks), {len(rp.bad)} decisions off a tie")
+    assert_replay(rp, g.q[:, o.perm], grid, cfg.grid, max_frac=max_frac,
+                  max_search_rows=max_search_rows)
+    return rp

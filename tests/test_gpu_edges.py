@@ -5,7 +5,7 @@ import pytest
 
 import oracle as O
 from post_weight_quantization_layer_amd import inputs as I
-from tests.gpu_harness import gpu_layer, log, oracle_layer
+from tests.gpu_harness import check_replay, gpu_layer, log, oracle_layer
 from tests.parity import assert_codes, classify_codes, rel_fro
 
 pytestmark = pytest.mark.gpu
@@ -103,6 +103,7 @@ def test_block_group_combinations(block, group):
     rep = classify_codes(g.q[:, o.perm], o.sweep, "affine", group)
     log(f"[edges] B={block} g={group}: {rep.mismatches} code mismatches")
     assert_codes(rep)
+    check_replay(cfg, W, o, g, tag=f"B={block} g={group}")
     assert rel_fro(g.U, o.U) <= 1e-4
 
 
@@ -117,6 +118,7 @@ def test_odd_width_small_groups(act):
     o, H, diag = oracle_layer(cfg, W.astype(np.float64), [I.bf16_to_f32(store[0])])
     rep = classify_codes(g.q[:, o.perm], o.sweep, "affine", 5)
     assert_codes(rep)
+    check_replay(cfg, W, o, g, tag=f"g=5 act={act}")
     assert rel_fro(g.U, o.U) <= 1e-4
     e_gpu = O.reconstruction_error(W, g.W_hat, H)
     e_or = O.reconstruction_error(W, o.what, H)
@@ -137,6 +139,7 @@ def test_bit_widths_and_per_channel(bits, group, block):
     rep = classify_codes(g.q[:, o.perm], o.sweep, "affine", group)
     log(f"[edges] bits={bits} g={group} B={block}: {rep.mismatches} code mismatches")
     assert_codes(rep)
+    check_replay(cfg, W, o, g, tag=f"bits={bits} g={group}")
     assert int(g.q.max()) <= 2 ** bits - 1
     e_gpu = O.reconstruction_error(W, g.W_hat, H)
     e_or = O.reconstruction_error(W, o.what, H)
@@ -161,6 +164,7 @@ def test_kquant_code_widths(bits, act):
     rep = classify_codes(qg_p, o.sweep, "q4k", 256)
     log(f"[edges] k-quant bits={bits}: {rep.mismatches} code mismatches")
     assert_codes(rep)
+    check_replay(cfg, W, o, g, tag=f"k-quant bits={bits}")
     kmax = 2 ** O.kquant_sub_bits(bits) - 1
     assert int(g.q.max()) <= 2 ** bits - 1
     assert int(g.sc.max()) <= kmax and int(g.mc.max()) <= kmax
@@ -181,11 +185,11 @@ def test_kquant_code_widths(bits, act):
 @pytest.mark.parametrize("bits,group,block,act", [(4, 128, 128, True), (3, 128, 64, True),
                                                   (4, 32, 128, False), (4, 256, 128, True)])
 def test_weighted_grid_search(bits, group, block, act):
-    """Importance-weighted grid choice: codes, scales and zero points as the
-    oracle's away from tie cascades (search ties included), the GPU's weights
-    on its own grid, reconstruction error within 1 % of the oracle's and
-    below the min-max grid's."""
-    from tests.parity import cascade_mask, near_half
+    """Importance-weighted grid choice: every GPU decision equals the
+    oracle's or is the other side of a tie (a rounding tie, or two candidate
+    scales of equal weighted error), through the tie-forced replay; the GPU's
+    weights on its own grid; reconstruction error within 1 % of the oracle's
+    and below the min-max grid's."""
     cfg = I.CONFIGS["down_proj_4096x11008_int4_g128_actorder"].with_(
         rows=96, cols=768, tokens=1800, bits=bits, group=group, block=block, act_order=act,
         x_kind="gauss", outlier_frac=0.01, outlier_scale=20.0)
@@ -196,21 +200,10 @@ def test_weighted_grid_search(bits, group, block, act):
     o, H, diag = oracle_layer(cfg, W.astype(np.float64), f32, search=True)
     perm = o.perm
     qg_p = g.q[:, perm]
-    rep = classify_codes(qg_p, o.sweep, "affine", group)
-    casc = cascade_mask(qg_p, o.sweep, group)
-    # a tie's cascade can move a later group's choice to another candidate,
-    # so the share of differing codes is counted outside the cascades
-    outside = (qg_p != o.sweep.q) & ~np.repeat(casc, group, axis=1)
-    log(f"[edges] search bits={bits} g={group}: {rep.mismatches} code mismatches in "
-        f"{rep.rows_with_mismatch} rows, {int(outside.sum())} outside tie cascades, "
-        f"{int((o.sweep.sgap < 1e-9).sum())} search ties")
-    assert not rep.unclassified, f"mismatches not at a tie: {rep.unclassified[:5]}"
-    assert outside.sum() == 0
-    assert rep.rows_with_mismatch <= max(1, qg_p.shape[0] // 50)
-    rel = np.abs(g.scale - o.sweep.scale) / o.sweep.scale
-    assert rel[~casc].max() <= 1e-3
-    zdiff = (g.zero.astype(np.int64) != o.sweep.zero.astype(np.int64)) & ~casc
-    assert np.all(near_half(o.sweep.zratio[zdiff], 1e-3))
+    log(f"[edges] search bits={bits} g={group}: {int((qg_p != o.sweep.q).sum())} codes differ "
+        f"from the oracle's, {int((o.sweep.sgap < 1e-9).sum())} search ties")
+    check_replay(cfg, W, o, g, diag=diag, search=True,
+                 max_search_rows=max(1, qg_p.shape[0] // 50), tag=f"search bits={bits} g={group}")
     s = np.repeat(g.scale, group, axis=1)
     z = np.repeat(g.zero.astype(np.float32), group, axis=1)
     np.testing.assert_array_equal(g.W_hat[:, perm], s * (qg_p.astype(np.float32) - z))
@@ -225,11 +218,13 @@ def test_weighted_grid_search(bits, group, block, act):
 
 @pytest.mark.parametrize("bits,act", [(4, True), (3, False)])
 def test_weighted_search_two_level_grid(bits, act):
-    """Importance-weighted (scale, min) of each sub-block of the two-level grid:
-    codes and grid codes as the oracle's outside tie cascades (search ties
-    included), weights on the GPU's own grid, reconstruction error within 1 %
-    of the oracle's and below the min-max grids'."""
-    from tests.parity import cascade_mask
+    """Importance-weighted (scale, min) of each sub-block of the two-level
+    grid: every GPU decision (fp16 super-scale and super-min, sub-block codes,
+    weight codes) equals the oracle's or is the other side of a tie, through
+    the tie-forced replay -- an fp16 super-scale may differ only where the
+    oracle's value lies within 1e-4 (relative) of the midpoint between the two
+    fp16 neighbours; weights on the GPU's own grid; reconstruction error
+    within 1 % of the oracle's and below the min-max grid's."""
     cfg = I.CONFIGS["q4k_14336x4096"].with_(rows=80, cols=768, tokens=1600, bits=bits,
                                               act_order=act, outlier_frac=0.01,
                                               outlier_scale=20.0)
@@ -240,23 +235,10 @@ def test_weighted_search_two_level_grid(bits, act):
     o, H, diag = oracle_layer(cfg, W.astype(np.float64), f32, search=True)
     perm = o.perm
     qg_p = g.q[:, perm]
-    rep = classify_codes(qg_p, o.sweep, "q4k", 256)
-    casc = cascade_mask(qg_p, o.sweep, O.Q4K_SUPER)
-    outside = (qg_p != o.sweep.q) & ~np.repeat(casc, O.Q4K_SUPER, axis=1)
-    log(f"[edges] two-level search bits={bits}: {rep.mismatches} code mismatches in "
-        f"{rep.rows_with_mismatch} rows, {int(outside.sum())} outside tie cascades")
-    assert not rep.unclassified, f"mismatches not at a tie: {rep.unclassified[:5]}"
-    assert outside.sum() == 0
-    assert rep.rows_with_mismatch <= max(1, qg_p.shape[0] // 50)
-    # super-scales within one fp16 step: the searched sub-block scales carry
-    # the last-bit differences of the fp32 trailing updates, which can move
-    # max_b s_b / kmax across an fp16 rounding boundary
-    for a_, b_ in ((g.D, o.sweep.D), (g.Dm, o.sweep.Dm)):
-        ga, ob = a_[~casc].astype(np.float32), b_[~casc].astype(np.float32)
-        assert np.all(np.abs(ga - ob) <= 2.0 ** -10 * np.abs(ob))
-    same = np.repeat((g.D == o.sweep.D) & (g.Dm == o.sweep.Dm) & ~casc, 8, axis=1)
-    np.testing.assert_array_equal(g.sc[same], o.sweep.sc[same])
-    np.testing.assert_array_equal(g.mc[same], o.sweep.mc[same])
+    log(f"[edges] two-level search bits={bits}: {int((qg_p != o.sweep.q).sum())} codes "
+        f"differ from the oracle's")
+    check_replay(cfg, W, o, g, diag=diag, search=True,
+                 max_search_rows=max(1, qg_p.shape[0] // 50), tag=f"two-level search bits={bits}")
     S = np.repeat(np.repeat(g.D.astype(np.float32), 8, axis=1) * g.sc, 32, axis=1)
     M = np.repeat(np.repeat(g.Dm.astype(np.float32), 8, axis=1) * g.mc, 32, axis=1)
     np.testing.assert_array_equal(g.W_hat[:, perm], S * qg_p.astype(np.float32) - M)
@@ -265,3 +247,59 @@ def test_weighted_search_two_level_grid(bits, act):
     assert abs(e_gpu - e_or) <= 0.01 * e_or
     base = gpu_layer(cfg, W, store)
     assert e_gpu < O.reconstruction_error(W, base.W_hat, H)
+
+
+def _near_tie_weights(rows, cols, group, bits, seed):
+    """Weights whose quotients w/s (float32, s the group's min-max scale, zero
+    point 0) lie 1.5e-5 to 3e-5 from a half-integer between 2^(bits-1) and
+    2^bits - 2, where w * (1/s) can round the other way; the first weight of
+    every group is its maximum.  Returns W and how many of its weights the
+    product w * (1/s) would round differently from the IEEE quotient."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    maxq = 2 ** bits - 1
+    W = np.zeros((rows, cols), f32)
+    flips = 0
+    for r in range(rows):
+        for g0 in range(0, cols, group):
+            M = f32(0.02 * (1.0 + rng.random()))
+            s = f32(M / f32(maxq))               # (xmax - 0) / maxq, as both sides form it
+            rs = f32(f32(1.0) / s)
+            W[r, g0] = M
+            k = g0 + 1
+            while k < g0 + group:
+                h = rng.integers(2 ** (bits - 1), maxq - 1) + 0.5
+                d = rng.uniform(1.5e-5, 3e-5) * rng.choice([-1.0, 1.0])
+                w = f32((h + d) * float(s))
+                q = float(f32(w / s))
+                if not 1.5e-5 <= abs(q - h) <= 3e-5:
+                    continue
+                flips += np.rint(f32(w * rs)) != np.rint(f32(w / s))
+                W[r, k] = w
+                k += 1
+    return W, int(flips)
+
+
+def test_eight_bit_codes_near_ties_are_exact():
+    """With a diagonal Hessian GPTQ is round-to-nearest (no compensation), so
+    the codes must equal the oracle's rint(w/s) bit for bit -- also for 8-bit
+    quotients near 255 lying a few float32 steps from a half-integer, where
+    w * (1/s) is known to round the other way for some of them."""
+    rows, cols, group, bits = 64, 256, 128, 8
+    cfg = I.CONFIGS["q_proj_4096x4096_int4_g128"].with_(rows=rows, cols=cols, tokens=1024,
+                                                       bits=bits, group=group, block=128,
+                                                       act_order=False)
+    W, flips = _near_tie_weights(rows, cols, group, bits, seed=11)
+    log(f"[edges] 8-bit near ties: the product rounds differently for {flips} weights")
+    assert flips > 0
+    X = np.zeros((cols, 1024), np.float32)
+    for i in range(cols):
+        X[i, 4 * i: 4 * i + 4] = 1.0 + (i % 5) / 8.0
+    store = [I.bf16_bits(X)]
+    g = gpu_layer(cfg, W, store)
+    o, H, diag = oracle_layer(cfg, W.astype(np.float64), [X])
+    assert np.all(np.triu(g.U, 1) == 0)
+    np.testing.assert_array_equal(g.scale, o.sweep.scale)
+    np.testing.assert_array_equal(g.zero.astype(np.float32), o.sweep.zero)
+    np.testing.assert_array_equal(g.q, o.q)
+    np.testing.assert_array_equal(g.W_hat, o.what)

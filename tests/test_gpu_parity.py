@@ -8,7 +8,7 @@ import pytest
 
 import oracle as O
 from post_weight_quantization_layer_amd import inputs as I
-from tests.gpu_harness import gpu_layer, log, oracle_layer
+from tests.gpu_harness import check_replay, gpu_layer, log, oracle_layer
 from tests.parity import assert_codes, cascade_mask, classify_codes, near_half, rel_fro
 
 pytestmark = pytest.mark.gpu
@@ -80,6 +80,9 @@ def test_codes_and_grid_parity(name):
     rep = classify_codes(qg_p, o.sweep, cfg.grid, cfg.group)
     log(f"[parity] {name} codes: {rep.mismatches}/{rep.n} differ in {rep.rows_with_mismatch} rows")
     assert_codes(rep)
+    # every GPU decision either equals the oracle's or is the other side of
+    # a tie, also inside a tie's cascade, and after the replay both agree
+    check_replay(cfg, W, o, g, tag=name)
     np.testing.assert_array_equal(g.g_idx, o.g_idx)
     if cfg.grid == "affine":
         casc = cascade_mask(qg_p, o.sweep, cfg.group)
