@@ -79,48 +79,77 @@ def measured_traffic(kernel):
     return m["bytes_per_launch"]
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def _blas() -> tuple[str, int]:
+    """BLAS library numpy calls and the threads it uses."""
+    try:
+        from threadpoolctl import threadpool_info
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            p = info[0]
+            return f"{p.get('internal_api')} {p.get('version')}", int(p.get("num_threads", 1))
+    except Exception:  # pragma: no cover
+        pass
+    return "unknown", os.cpu_count() or 1
+
+
 def cpu_baseline(cfg, chunk_tokens):
     """The float64 oracle, as it stands, on a bounded sample of the same
     workload, scaled to milliseconds per layer with the cost model of the
     pages (H linear in tokens, the inverse factor cubic in d, the sweep and
-    packing linear in rows)."""
+    packing linear in rows).  Each part is timed on a sample large enough
+    that its per-call overheads are amortized: one 8192-token chunk of X,
+    the leading d/2 block of H, 256 rows of W over all columns."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    blas, threads = _blas()
     d, r = cfg.cols, cfg.rows
-    ntok = 1024
+    ntok = min(8192, cfg.tokens)
     x = I.x_chunk(cfg, 0, ntok)
     t0 = time.perf_counter()
     H = O.hessian([x])
     diag = O.hessian_diag([x])
-    t_h = (time.perf_counter() - t0) * (cfg.tokens / ntok)
-    ds = d // 4
+    t_h = time.perf_counter() - t0
+    del x
+    ds = max(d // 2, 1)
     t0 = time.perf_counter()
     perm = O.act_order_perm(diag[:ds]) if cfg.act_order else np.arange(ds)
     Hp = O.damped_processing_hessian(H[:ds, :ds], diag[:ds], perm, cfg.percdamp)
     O.inverse_cholesky_upper(Hp)
-    t_u = (time.perf_counter() - t0) * (d / ds) ** 3
+    t_u = time.perf_counter() - t0
     del H, Hp
-    nrow = 8
+    nrow = min(256, r)
     W = I.weight_rows(cfg, np.arange(nrow)).astype(np.float64)
     U = np.eye(d)   # the sweep's cost does not depend on U's values
     t0 = time.perf_counter()
     sw = O.gptq_sweep(W, U, O.GridSpec(cfg.grid, cfg.bits, cfg.group))
-    t_s = (time.perf_counter() - t0) * (r / nrow)
+    t_s = time.perf_counter() - t0
     t0 = time.perf_counter()
     O.pack(sw.q.astype(np.int64), cfg.bits)
-    t_p = (time.perf_counter() - t0) * (r / nrow)
-    total_ms = (t_h + t_u + t_s + t_p) * 1e3
+    t_p = time.perf_counter() - t0
+    scale = {"hessian": cfg.tokens / ntok, "inverse_factor": (d / ds) ** 3,
+             "sweep": r / nrow, "pack": r / nrow}
+    meas = {"hessian": t_h, "inverse_factor": t_u, "sweep": t_s, "pack": t_p}
+    split = {k: round(meas[k] * scale[k] * 1e3, 1) for k in meas}
+    total_ms = sum(split.values())
     return {"value": round(total_ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
-            "sample": (f"H on {ntok} of {cfg.tokens} tokens (x{cfg.tokens // ntok}); damping, "
-                       f"act-order and inverse factor on the leading {ds}x{ds} block "
-                       f"(x(d/{ds})^3); sweep and pack over all {d} columns of {nrow} of {r} "
-                       f"rows (x{r // nrow}); float64 numpy/OpenBLAS"),
-            "split_ms": {"hessian": round(t_h * 1e3, 1), "inverse_factor": round(t_u * 1e3, 1),
-                         "sweep": round(t_s * 1e3, 1), "pack": round(t_p * 1e3, 1)}}
+            "extrapolated": True,
+            "sample": (f"H on {ntok} of {cfg.tokens} tokens; damping, act-order and inverse "
+                       f"factor on the leading {ds}x{ds} block; sweep and pack over all {d} "
+                       f"columns of {nrow} of {r} rows; each part scaled by its cost model "
+                       f"(tokens, d^3, rows); float64 numpy"),
+            "measured_s": {k: round(v, 2) for k, v in meas.items()},
+            "scale": {k: round(v, 3) for k, v in scale.items()},
+            "split_ms": split, "cpu_model": _cpu_model(), "blas": blas}
 
 
 # W4A16 product workloads: the shapes of the quantization workloads, stored as
