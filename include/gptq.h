@@ -325,6 +325,33 @@ gptq_status gptq_w4a16_gemm(const gptq_w4a16_layer *layer, const uint16_t *x,
                             int64_t batch, uint16_t *y, void *ws,
                             size_t ws_bytes, void *stream);
 
+/* Size of the static device scratch of gptq_w4a16_gemm_noalloc (per GPU). */
+#define GPTQ_W4A16_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * y = x W^T exactly as gptq_w4a16_gemm computes it (same kernels, same
+ * bits), for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace and calls no allocator; its scratch memory (the
+ * gathered activations of an activation-ordered layer, split-K partial
+ * sums) is a static device array of GPTQ_W4A16_STATIC_SCRATCH_BYTES inside
+ * the library, one per GPU, held from the library's load until the process
+ * ends.  Its address on a device is looked up once, on the first call on
+ * that device.
+ *
+ * Every call on a GPU shares that GPU's array, and each call writes its
+ * scratch in full before reading it (nothing in it needs to start at zero).
+ * Calls whose execution overlaps on one GPU -- on different streams, or
+ * from different host threads without ordering -- race on the array and
+ * must not be issued; calls on one stream are ordered and safe.
+ *
+ * Arguments as for gptq_w4a16_gemm.  Returns GPTQ_ERR_WORKSPACE, with
+ * nothing enqueued, when gptq_w4a16_workspace_bytes(layer, batch) exceeds
+ * GPTQ_W4A16_STATIC_SCRATCH_BYTES (large batches on wide layers).
+ */
+gptq_status gptq_w4a16_gemm_noalloc(const gptq_w4a16_layer *layer, const uint16_t *x,
+                                    int64_t batch, uint16_t *y, void *stream);
+
 /*
  * Per-kernel timing with HIP events (for measurement, off by default).
  * When enabled, every kernel launch of the library is bracketed by a pair of

@@ -24,7 +24,7 @@ EXPORTED = (
     "gptq_profile_enable", "gptq_profile_reset", "gptq_profile_query",
     "gptq_w4a16_layer_bytes", "gptq_w4a16_prepare", "gptq_w4a16_workspace_bytes",
     "gptq_w4a16_gemm", "gptq_linear_forward_ws_bytes", "gptq_linear_forward",
-    "gptq_silu_mul",
+    "gptq_silu_mul", "gptq_w4a16_gemm_noalloc",
 )
 
 
@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
     L.gptq_w4a16_workspace_bytes.argtypes = [ctypes.POINTER(gptq_w4a16_layer), I64]
     L.gptq_w4a16_gemm.restype = I32
     L.gptq_w4a16_gemm.argtypes = [ctypes.POINTER(gptq_w4a16_layer), P, I64, P, P, SZ, P]
+    L.gptq_w4a16_gemm_noalloc.restype = I32
+    L.gptq_w4a16_gemm_noalloc.argtypes = [ctypes.POINTER(gptq_w4a16_layer), P, I64, P, P]
     L.gptq_linear_forward_ws_bytes.restype = SZ
     L.gptq_linear_forward_ws_bytes.argtypes = [I64, I64, I64]
     L.gptq_linear_forward.restype = I32
@@ -205,6 +207,14 @@ def gptq_w4a16_prepare(packed, g_idx, scale, zero_packed, rows: int, cols: int, 
 
 def gptq_w4a16_workspace_bytes(layer: gptq_w4a16_layer, batch: int) -> int:
     return lib().gptq_w4a16_workspace_bytes(ctypes.byref(layer), batch)
+
+
+def gptq_w4a16_gemm_noalloc(layer: gptq_w4a16_layer, x, y, batch: int | None = None,
+                            stream=None):
+    """As gptq_w4a16_gemm, with the library's static device scratch (no workspace)."""
+    b = x.shape[0] if batch is None else batch
+    _check(lib().gptq_w4a16_gemm_noalloc(ctypes.byref(layer), _ptr(x), b, _ptr(y),
+                                         _stream(stream)))
 
 
 def gptq_w4a16_gemm(layer: gptq_w4a16_layer, x, y, ws=None, batch: int | None = None,

@@ -27,6 +27,8 @@
 // (exact in fp32) and sums in fp32; the group's scale is applied to that sum.
 #include <algorithm>
 #include <cmath>
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -702,6 +704,117 @@ gptq_status launch_rows_sps(const W4Args &a, const RowsPlan &r, int sps, hipStre
   }
 }
 
+// ------------------------------------------------- no-allocation product
+// Scratch memory of gptq_w4a16_gemm_noalloc: a static device array, one copy
+// per GPU the library runs on, held until the process ends.  Its host-side
+// name is only a handle: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept.
+constexpr size_t kScratchBytes = GPTQ_W4A16_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch_ptr;   // device -> address of its `scratch`
+
+gptq_status scratch_address(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(GPTQ_ERR_DEVICE, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *out = it->second;
+    return GPTQ_OK;
+  }
+  void *ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || ptr == nullptr)
+    return fail(GPTQ_ERR_DEVICE, std::string("cannot locate the static scratch on device ") +
+                                     std::to_string(dev) + ": " + hipGetErrorString(e));
+  g_scratch_ptr[dev] = ptr;
+  *out = ptr;
+  return GPTQ_OK;
+}
+
+// Argument checks shared by both products (host only, before any launch).
+gptq_status check_gemm_args(const gptq_w4a16_layer *layer, const uint16_t *x, int64_t batch,
+                            const uint16_t *y) {
+  if (!layer || !layer->mem) return fail(GPTQ_ERR_INVALID_ARG, "layer is not prepared");
+  if (batch < 1 || batch > 4096) return fail(GPTQ_ERR_INVALID_ARG, "batch must be in [1, 4096]");
+  if (!x || !y) return fail(GPTQ_ERR_INVALID_ARG, "x and y must not be NULL");
+  if (reinterpret_cast<uintptr_t>(x) % 16)
+    return fail(GPTQ_ERR_INVALID_ARG, "x must be 16-byte aligned");
+  if (!valid_group(layer->cols, layer->group) || layer->rows < 1)
+    return fail(GPTQ_ERR_INVALID_ARG, "layer is not prepared");
+  return GPTQ_OK;
+}
+
+// The product's launches, arguments already checked and `ws` large enough.
+gptq_status gemm_launches(const gptq_w4a16_layer *layer, const uint16_t *x, int64_t batch,
+                          uint16_t *y, void *ws, hipStream_t s) {
+  const Geometry g = geometry(layer->rows, layer->cols, layer->group);
+  const LayerMap m = layer_map(layer->mem, g);
+  const int cus = cu_count();
+  uint16_t *xp = layer->permuted ? static_cast<uint16_t *>(ws) : nullptr;
+  float *part = reinterpret_cast<float *>(
+      static_cast<char *>(ws) +
+      (layer->permuted ? align256(sizeof(uint16_t) * std::min<int64_t>(batch, kMaxBatch) * g.k_pad)
+                       : 0));
+  const int sps = g.group >= kStep ? 1 : kStep / g.group;
+  for (int64_t b0 = 0; b0 < batch; b0 += kMaxBatch) {
+    const int bc = int(std::min<int64_t>(kMaxBatch, batch - b0));
+    W4Args a;
+    a.x = x + b0 * g.cols;
+    a.ldx = g.cols;
+    if (layer->permuted) {
+      const int64_t total = int64_t(bc) * g.k_pad / 8;
+      GPTQ_TRY(launch("w4a16_gather_x", w4a16_gather_x_kernel, dim3(cdiv(total, kThreads)),
+                      dim3(kThreads), 0, s, a.x, g.cols, g.k_pad, total,
+                      (const int32_t *)m.kperm, xp));
+      a.x = xp;
+      a.ldx = g.k_pad;
+    }
+    a.wq = m.wq;
+    a.sc = m.sc;
+    a.zp = m.zp;
+    a.y = y + b0 * g.rows;
+    a.part = part;
+    a.ldy = g.rows;
+    a.batch = bc;
+    a.cols = int32_t(g.cols);
+    a.rows = int32_t(g.rows);
+    a.rows_pad = int32_t(g.rows_pad);
+    a.rt16 = int32_t(g.rt16);
+    a.ksteps = int32_t(g.ksteps);
+    a.ngp = int32_t(g.ngp);
+    a.gsteps = g.group >= kStep ? g.group / kStep : 1;
+    const RowsPlan rp = rows_plan(g, bc, cus);
+    if (rp.waves) {
+      a.splits = 1;
+      a.base = a.rem = a.ns_max = 0;
+      GPTQ_TRY(launch_rows_sps(a, rp, sps, s));
+      continue;
+    }
+    const W4Plan p = plan_for(g, bc, cus);
+    a.splits = p.splits;
+    a.base = p.base;
+    a.rem = p.rem;
+    a.ns_max = p.ns_max;
+    switch (p.mt) {
+      case 1: GPTQ_TRY(launch_gemm_sps<1>(a, p, sps, s)); break;
+      case 2: GPTQ_TRY(launch_gemm_sps<2>(a, p, sps, s)); break;
+      case 3: GPTQ_TRY(launch_gemm_sps<3>(a, p, sps, s)); break;
+      default: GPTQ_TRY(launch_gemm_sps<4>(a, p, sps, s)); break;
+    }
+    if (p.splits > 1) {
+      const int64_t total = int64_t(bc) * g.rows;
+      GPTQ_TRY(launch("w4a16_reduce", w4a16_reduce_kernel, dim3(cdiv(total, kThreads)),
+                      dim3(kThreads), 0, s, (const float *)part, int32_t(p.splits), int32_t(bc),
+                      int32_t(g.rows), int32_t(g.rows_pad), a.y, int64_t(g.rows)));
+    }
+  }
+  return GPTQ_OK;
+}
+
 }  // namespace
 }  // namespace gptq
 
@@ -775,17 +888,9 @@ size_t gptq_w4a16_workspace_bytes(const gptq_w4a16_layer *layer, int64_t batch) 
 
 gptq_status gptq_w4a16_gemm(const gptq_w4a16_layer *layer, const uint16_t *x, int64_t batch,
                             uint16_t *y, void *ws, size_t ws_bytes, void *stream) {
-  if (!layer || !layer->mem) return fail(GPTQ_ERR_INVALID_ARG, "layer is not prepared");
-  if (batch < 1 || batch > 4096) return fail(GPTQ_ERR_INVALID_ARG, "batch must be in [1, 4096]");
-  if (!x || !y) return fail(GPTQ_ERR_INVALID_ARG, "x and y must not be NULL");
-  if (reinterpret_cast<uintptr_t>(x) % 16)
-    return fail(GPTQ_ERR_INVALID_ARG, "x must be 16-byte aligned");
-  if (!valid_group(layer->cols, layer->group) || layer->rows < 1)
-    return fail(GPTQ_ERR_INVALID_ARG, "layer is not prepared");
+  GPTQ_TRY(check_gemm_args(layer, x, batch, y));
   const Geometry g = geometry(layer->rows, layer->cols, layer->group);
-  const LayerMap m = layer_map(layer->mem, g);
-  const int cus = cu_count();
-  const size_t need = ws_bytes_for(g, layer->permuted != 0, batch, cus);
+  const size_t need = ws_bytes_for(g, layer->permuted != 0, batch, cu_count());
   if (need) {
     if (!ws) return fail(GPTQ_ERR_WORKSPACE, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(ws) % 256)
@@ -794,66 +899,22 @@ gptq_status gptq_w4a16_gemm(const gptq_w4a16_layer *layer, const uint16_t *x, in
       return fail(GPTQ_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) +
                                           " bytes, got " + std::to_string(ws_bytes));
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint16_t *xp = layer->permuted ? static_cast<uint16_t *>(ws) : nullptr;
-  float *part = reinterpret_cast<float *>(
-      static_cast<char *>(ws) +
-      (layer->permuted ? align256(sizeof(uint16_t) * std::min<int64_t>(batch, kMaxBatch) * g.k_pad)
-                       : 0));
-  const int sps = g.group >= kStep ? 1 : kStep / g.group;
-  for (int64_t b0 = 0; b0 < batch; b0 += kMaxBatch) {
-    const int bc = int(std::min<int64_t>(kMaxBatch, batch - b0));
-    W4Args a;
-    a.x = x + b0 * g.cols;
-    a.ldx = g.cols;
-    if (layer->permuted) {
-      const int64_t total = int64_t(bc) * g.k_pad / 8;
-      GPTQ_TRY(launch("w4a16_gather_x", w4a16_gather_x_kernel, dim3(cdiv(total, kThreads)),
-                      dim3(kThreads), 0, s, a.x, g.cols, g.k_pad, total,
-                      (const int32_t *)m.kperm, xp));
-      a.x = xp;
-      a.ldx = g.k_pad;
-    }
-    a.wq = m.wq;
-    a.sc = m.sc;
-    a.zp = m.zp;
-    a.y = y + b0 * g.rows;
-    a.part = part;
-    a.ldy = g.rows;
-    a.batch = bc;
-    a.cols = int32_t(g.cols);
-    a.rows = int32_t(g.rows);
-    a.rows_pad = int32_t(g.rows_pad);
-    a.rt16 = int32_t(g.rt16);
-    a.ksteps = int32_t(g.ksteps);
-    a.ngp = int32_t(g.ngp);
-    a.gsteps = g.group >= kStep ? g.group / kStep : 1;
-    const RowsPlan rp = rows_plan(g, bc, cus);
-    if (rp.waves) {
-      a.splits = 1;
-      a.base = a.rem = a.ns_max = 0;
-      GPTQ_TRY(launch_rows_sps(a, rp, sps, s));
-      continue;
-    }
-    const W4Plan p = plan_for(g, bc, cus);
-    a.splits = p.splits;
-    a.base = p.base;
-    a.rem = p.rem;
-    a.ns_max = p.ns_max;
-    switch (p.mt) {
-      case 1: GPTQ_TRY(launch_gemm_sps<1>(a, p, sps, s)); break;
-      case 2: GPTQ_TRY(launch_gemm_sps<2>(a, p, sps, s)); break;
-      case 3: GPTQ_TRY(launch_gemm_sps<3>(a, p, sps, s)); break;
-      default: GPTQ_TRY(launch_gemm_sps<4>(a, p, sps, s)); break;
-    }
-    if (p.splits > 1) {
-      const int64_t total = int64_t(bc) * g.rows;
-      GPTQ_TRY(launch("w4a16_reduce", w4a16_reduce_kernel, dim3(cdiv(total, kThreads)),
-                      dim3(kThreads), 0, s, (const float *)part, int32_t(p.splits), int32_t(bc),
-                      int32_t(g.rows), int32_t(g.rows_pad), a.y, int64_t(g.rows)));
-    }
-  }
-  return GPTQ_OK;
+  return gemm_launches(layer, x, batch, y, ws, static_cast<hipStream_t>(stream));
+}
+
+gptq_status gptq_w4a16_gemm_noalloc(const gptq_w4a16_layer *layer, const uint16_t *x,
+                                    int64_t batch, uint16_t *y, void *stream) {
+  GPTQ_TRY(check_gemm_args(layer, x, batch, y));
+  const Geometry g = geometry(layer->rows, layer->cols, layer->group);
+  const size_t need = ws_bytes_for(g, layer->permuted != 0, batch, cu_count());
+  if (need > kScratchBytes)
+    return fail(GPTQ_ERR_WORKSPACE,
+                "this product needs " + std::to_string(need) + " bytes of scratch; the static "
+                "scratch holds " + std::to_string(kScratchBytes) +
+                " (use a smaller batch, or gptq_w4a16_gemm with a workspace)");
+  void *ws = nullptr;
+  if (need) GPTQ_TRY(scratch_address(&ws));
+  return gemm_launches(layer, x, batch, y, ws, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -21,7 +21,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = B.lib()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.EXPORTED)
@@ -164,6 +164,26 @@ def test_w4a16_gemm_rejects_before_any_launch():
         B.GPTQ_ERR_WORKSPACE
     assert L.gptq_w4a16_gemm(ctypes.byref(lay), FAKE, 16, FAKE, FAKE, need - 1, None) == \
         B.GPTQ_ERR_WORKSPACE
+
+
+def test_w4a16_noalloc_rejects_before_any_launch():
+    """The no-allocation product checks its arguments, and that the product
+    fits the static scratch, on the host before any HIP call."""
+    L = B.lib()
+    empty = B.gptq_w4a16_layer()
+    assert L.gptq_w4a16_gemm_noalloc(ctypes.byref(empty), FAKE, 1, FAKE, None) == \
+        B.GPTQ_ERR_INVALID_ARG
+    # an activation-ordered layer with 2^20 input features: 64 gathered rows
+    # of x alone take 128 MiB
+    lay = B.gptq_w4a16_layer(rows=4096, cols=1 << 20, group=128, permuted=1, rows_pad=4096,
+                             k_pad=1 << 20, mem=0x10000, mem_bytes=1 << 34)
+    need = B.gptq_w4a16_workspace_bytes(lay, 64)
+    assert need > 32 << 20
+    assert L.gptq_w4a16_gemm_noalloc(ctypes.byref(lay), FAKE, 64, FAKE, None) == \
+        B.GPTQ_ERR_WORKSPACE
+    assert "static scratch" in B.gptq_last_error()
+    assert L.gptq_w4a16_gemm_noalloc(ctypes.byref(lay), FAKE, 0, FAKE, None) == \
+        B.GPTQ_ERR_INVALID_ARG
 
 
 def test_weighted_search_needs_hdiag():
