@@ -101,8 +101,9 @@ typedef struct {
 const char *gptq_last_error(void);
 
 /* Bytes of `ws` needed by gptq_prepare_hinv (for cols) and by
- * gptq_quantize_layer (for rows x cols) with these parameters; the larger of
- * the two, so one buffer serves both calls.  Returns 0 on invalid arguments. */
+ * gptq_quantize_layer (for rows x cols) with these parameters, and wanted by
+ * gptq_hessian_accumulate (for cols features); the largest of the three, so
+ * one buffer serves all three calls.  Returns 0 on invalid arguments. */
 size_t gptq_workspace_bytes(int64_t rows, int64_t cols, const gptq_params *p);
 
 /*
@@ -123,12 +124,21 @@ size_t gptq_workspace_bytes(int64_t rows, int64_t cols, const gptq_params *p);
  *         (ld_x >= n_tok), dtype x_dtype (BF16 = raw bfloat16 bits, or
  *         F32).  16-byte aligned, and ld_x a multiple of 8 (BF16) or 4 (F32).
  *  n_tok  tokens in this chunk (0 is a no-op).
+ *  ws     optional scratch (NULL with ws_bytes 0, or 256-byte aligned): with
+ *         room for it, the bf16 path splits the tiles of its last, partly
+ *         filled round of workgroups into token parts whose sums are added
+ *         into H in a fixed order, so that the round fills the GPU.  More
+ *         room allows finer parts, up to what gptq_workspace_bytes asks for
+ *         and beyond; none at all gives one workgroup per tile.
  *
- * Products of bf16 inputs are exact in float32; sums are float32 in H.
+ * Products of bf16 inputs are exact in float32; sums are float32 in H.  For
+ * given sizes, compute-unit count and ws_bytes the result is the same bits
+ * on every call.
  */
 gptq_status gptq_hessian_accumulate(float *H, double *hdiag, int64_t d,
                                     const void *X, int32_t x_dtype,
-                                    int64_t n_tok, int64_t ld_x, void *stream);
+                                    int64_t n_tok, int64_t ld_x, void *ws,
+                                    size_t ws_bytes, void *stream);
 
 /*
  * Damping, order and inverse-Hessian factor.

@@ -77,7 +77,7 @@ def lib() -> ctypes.CDLL:
     L.gptq_workspace_bytes.restype = SZ
     L.gptq_workspace_bytes.argtypes = [I64, I64, ctypes.POINTER(gptq_params)]
     L.gptq_hessian_accumulate.restype = I32
-    L.gptq_hessian_accumulate.argtypes = [P, P, I64, P, I32, I64, I64, P]
+    L.gptq_hessian_accumulate.argtypes = [P, P, I64, P, I32, I64, I64, P, SZ, P]
     L.gptq_prepare_hinv.restype = I32
     L.gptq_prepare_hinv.argtypes = [P, P, I64, ctypes.POINTER(gptq_params), P, P, P, P, SZ, P]
     L.gptq_quantize_layer.restype = I32
@@ -146,8 +146,9 @@ def gptq_workspace_bytes(rows: int, cols: int, params: gptq_params) -> int:
 
 
 def gptq_hessian_accumulate(H, hdiag, X, n_tok: int | None = None, ld_x: int | None = None,
-                            stream=None):
-    """H (d x d fp32), hdiag (d fp64), X (d x n) bf16 or fp32 (device tensors)."""
+                            ws=None, stream=None):
+    """H (d x d fp32), hdiag (d fp64), X (d x n) bf16 or fp32 (device tensors);
+    ws: optional uint8 device scratch."""
     import torch
     d = H.shape[0]
     if X.dtype == torch.bfloat16:
@@ -158,8 +159,9 @@ def gptq_hessian_accumulate(H, hdiag, X, n_tok: int | None = None, ld_x: int | N
         raise TypeError("X must be bfloat16 or float32")
     n = X.shape[1] if n_tok is None else n_tok
     ld = X.stride(0) if ld_x is None else ld_x
-    _check(lib().gptq_hessian_accumulate(_ptr(H), _ptr(hdiag), d, _ptr(X), dt, n, ld,
-                                         _stream(stream)))
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gptq_hessian_accumulate(_ptr(H), _ptr(hdiag), d, _ptr(X), dt, n, ld, _ptr(ws),
+                                         nbytes, _stream(stream)))
 
 
 def gptq_prepare_hinv(H, hdiag, params: gptq_params, U, perm, dead, ws, stream=None):

@@ -56,7 +56,7 @@ class GatedMLPCalibrator:
         dn.reset_hessian()
         for X in x_chunks:                            # 1. activations reaching gate/up
             B.gptq_hessian_accumulate(gu.H, gu.hdiag, X, n_tok=X.shape[1],
-                                      ld_x=X.stride(0), stream=stream)
+                                      ld_x=X.stride(0), ws=gu.ws, stream=stream)
         gu.prepare(stream=stream)                     # 2. update gate and up
         q_gate = gu.quantize(W_gate, stream=stream)
         q_up = gu.quantize(W_up, stream=stream)
@@ -73,7 +73,7 @@ class GatedMLPCalibrator:
             A = _bf16_buffer(self.d_ff, n, self.device)
             B.gptq_silu_mul(G, Uo, A, n_tok=n, stream=stream)
             B.gptq_hessian_accumulate(dn.H, dn.hdiag, A, n_tok=n, ld_x=A.stride(0),
-                                      stream=stream)  # 4. activations reaching down
+                                      ws=dn.ws, stream=stream)  # 4. activations reaching down
             acts.append(A[:, :n])
         dn.prepare(stream=stream)
         q_down = dn.quantize(W_down, stream=stream)

@@ -1,5 +1,6 @@
 // C ABI entry points: argument validation (host only, before any launch),
 // thread-local error text, and the event-based per-kernel profiler.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -190,14 +191,15 @@ size_t gptq_workspace_bytes(int64_t rows, int64_t cols, const gptq_params *p) {
     return 0;
   }
   if (check_params(p, cols) != GPTQ_OK) return 0;
-  size_t a = prepare_ws_bytes(cols);
-  size_t b = quantize_ws_bytes(rows, cols, *p);
-  return a > b ? a : b;
+  const size_t a = prepare_ws_bytes(cols);
+  const size_t b = quantize_ws_bytes(rows, cols, *p);
+  const size_t h = hessian_ws_bytes(cols);
+  return std::max(a, std::max(b, h));
 }
 
 gptq_status gptq_hessian_accumulate(float *H, double *hdiag, int64_t d, const void *X,
-                                    int32_t x_dtype, int64_t n_tok, int64_t ld_x,
-                                    void *stream) {
+                                    int32_t x_dtype, int64_t n_tok, int64_t ld_x, void *ws,
+                                    size_t ws_bytes, void *stream) {
   if (d < 1 || d > kMaxDim) return fail(GPTQ_ERR_INVALID_ARG, "d must be in [1, 2^20]");
   if (!H || !hdiag) return fail(GPTQ_ERR_INVALID_ARG, "H and hdiag must not be NULL");
   if (x_dtype != GPTQ_DT_F32 && x_dtype != GPTQ_DT_BF16)
@@ -213,7 +215,10 @@ gptq_status gptq_hessian_accumulate(float *H, double *hdiag, int64_t d, const vo
     return fail(GPTQ_ERR_INVALID_ARG, "ld_x must be a multiple of 4 for f32 X");
   if (!aligned(H, 16) || !aligned(hdiag, 8))
     return fail(GPTQ_ERR_INVALID_ARG, "H must be 16-byte and hdiag 8-byte aligned");
-  return hessian_accumulate_impl(H, hdiag, d, X, x_dtype, n_tok, ld_x, (hipStream_t)stream);
+  if (ws && !aligned(ws, 256))
+    return fail(GPTQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return hessian_accumulate_impl(H, hdiag, d, X, x_dtype, n_tok, ld_x, ws, ws ? ws_bytes : 0,
+                                 (hipStream_t)stream);
 }
 
 gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d,

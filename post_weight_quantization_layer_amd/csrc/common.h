@@ -89,8 +89,9 @@ gptq_status gemm_f32(const float *A, int64_t lda, const float *B, int64_t ldb, f
 
 // ----------------------------------------------------------- step drivers
 gptq_status hessian_accumulate_impl(float *H, double *hdiag, int64_t d, const void *X,
-                                    int x_dtype, int64_t n_tok, int64_t ld_x,
-                                    hipStream_t stream);
+                                    int x_dtype, int64_t n_tok, int64_t ld_x, void *ws,
+                                    size_t ws_bytes, hipStream_t stream);
+size_t hessian_ws_bytes(int64_t d);
 gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
                               const gptq_params &p, float *U, int32_t *perm, uint8_t *dead,
                               void *ws, size_t ws_bytes, hipStream_t stream);

@@ -2,10 +2,13 @@
 // float64 activation energy hdiag += 2 sum_t x_it^2.
 //
 // bf16 path: a SYRK on bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 accumulate.
-// Only the upper-triangle 256x256 tiles of H are computed.  Each tile is
+// Only the upper-triangle 256x256 tiles of H are computed.  Most tiles are
 // owned by one workgroup that runs the whole token loop, so H is updated by
-// one read-modify-write per tile and the result is deterministic (no split-K
-// atomics).  X is d x n row-major (tokens contiguous), so both MFMA operands
+// one read-modify-write per tile.  The tiles of the last, partly filled
+// round may instead be split into `parts` token ranges run by different
+// workgroups: part 0 adds into H, parts 1.. store their sums into workspace
+// slots, and a second kernel adds the slots into H in part order, so the
+// result is deterministic (no split-K atomics).  X is d x n row-major (tokens contiguous), so both MFMA operands
 // are K-contiguous rows of X and no transpose is needed anywhere.  X panels
 // stream through registers into a double-buffered LDS ring; on diagonal
 // tiles the four waves also accumulate the float64 activation energy of the
@@ -20,6 +23,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int kTile = 256;       // H tile edge
@@ -113,20 +117,55 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) {
   return (double)__uint_as_float(bits16 << 16);
 }
 
+// Work of one XCD.  Workgroups are dealt round-robin to the 8 XCDs, so each
+// XCD gets a contiguous run of the tile order (tiles that share X panels
+// share that XCD's L2): tiles [first, first + full + tail).  Its `cus`
+// compute units take the `full` tiles in whole rounds; the `tail` tiles of
+// the last, partly filled round are split into token parts.
+struct XcdRun {
+  int first, full, tail;
+};
+__host__ __device__ inline XcdRun xcd_run(int x, int ntiles, int cus) {
+  const int f = (x * ntiles) / 8, r = ((x + 1) * ntiles) / 8 - f;
+  const int full = (r % cus == 0) ? r : (r / cus) * cus;
+  return {f, full, r - full};
+}
+
+// Workspace slot of a split tile's part p >= 1: its 256 x 256 sums (2 X X^T
+// over the part's tokens, row-major), then, for a diagonal tile, the 256
+// rows' float64 energies.
+constexpr int64_t kSlotFloats = int64_t(kTile) * kTile + 2 * kTile;
+constexpr size_t kSlotBytes = size_t(kSlotFloats) * sizeof(float);
+
 // One workgroup per CU (128 KB of LDS) and one wave per SIMD: the kernel may
 // use the whole register file, so both fragment sets stay in registers.
+// Workgroup (xcd, slot): slot < full -> whole tile first + slot; else unit
+// u = slot - full, part u / tail of tile first + full + u % tail (parts
+// outermost, so that concurrent units read the same token range of
+// neighbouring tiles).
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
     syrk_bf16_kernel(float *__restrict__ H, double *__restrict__ hdiag,
                      const uint16_t *__restrict__ X, int64_t d, int64_t n, int64_t ld, int nt,
-                     int ntiles, int per_xcd) {
-  // XCD-aware mapping: workgroups are dealt round-robin to the 8 XCDs, so
-  // give each XCD a contiguous run of the tile order (shared panels stay in
-  // that XCD's L2).
+                     int ntiles, int parts, int xcd_cus, float *__restrict__ slots) {
   const int bid = blockIdx.x;
   const int xcd = bid & 7, slot = bid >> 3;
-  if (slot >= per_xcd) return;
-  const int t = xcd * per_xcd + slot;
-  if (t >= ntiles) return;
+  const XcdRun run = xcd_run(xcd, ntiles, xcd_cus);
+  int t, part = 0, nparts = 1;   // this unit: part `part` of `nparts` token ranges
+  float *dst_slot = nullptr;
+  if (slot < run.full) {
+    t = run.first + slot;
+  } else {
+    nparts = parts;
+    const int u = slot - run.full;
+    if (u >= run.tail * parts) return;
+    part = u / run.tail;
+    t = run.first + run.full + u % run.tail;
+    if (part > 0) {
+      int gi = u % run.tail;             // index among all XCDs' tail tiles
+      for (int x = 0; x < xcd; ++x) gi += xcd_run(x, ntiles, xcd_cus).tail;
+      dst_slot = slots + (int64_t(gi) * (parts - 1) + part - 1) * kSlotFloats;
+    }
+  }
   int ti, tj;
   tile_coords(t, nt, ti, tj);
   const bool diag = ti == tj;
@@ -159,7 +198,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
   // row's 128 contiguous bytes (a whole cache line).  Stages past the last
   // full one re-load that one; that extra copy lands in a slot the tail
   // path overwrites.
+  // this unit's full 64-token stages [ks0, ks1); the ragged token tail goes
+  // with the last part
   const int64_t nfull = n / kBK;
+  const int64_t ks0 = nfull * part / nparts, ks1 = nfull * (part + 1) / nparts;
+  const bool has_tail = part == nparts - 1 && nfull * kBK < n;
   const int lrow = tid >> 3, lchunk = tid & 7;
   const int lds_off = lrow * kRowBytes + ((lchunk ^ swz(lrow)) << 4);
   const uint16_t *rp[kLoads];
@@ -169,7 +212,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
             lchunk * 8;
   u32x4_t stg[kLoads];
   auto load_one = [&](int q, int64_t ks) {
-    stg[q] = *reinterpret_cast<const u32x4_t *>(rp[q] + min(ks, nfull - 1) * kBK);
+    stg[q] = *reinterpret_cast<const u32x4_t *>(rp[q] + min(ks, ks1 - 1) * kBK);
   };
   auto store_one = [&](int q, int64_t ks) {
     *reinterpret_cast<u32x4_t *>(smem + (ks % kStages) * kStageBytes + lds_off +
@@ -247,13 +290,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
     tail_panel(X, ld, d, n, J0, nfull * kBK, base + kPanelBytes, tid);
     __syncthreads();
   };
-  if (nfull > 0) {
+  if (ks1 > ks0) {
 #pragma unroll
-    for (int q = 0; q < kLoads; ++q) load_one(q, 0);
+    for (int q = 0; q < kLoads; ++q) load_one(q, ks0);
 #pragma unroll
-    for (int q = 0; q < kLoads; ++q) store_one(q, 0);
+    for (int q = 0; q < kLoads; ++q) store_one(q, ks0);
 #pragma unroll
-    for (int q = 0; q < kLoads; ++q) load_one(q, 1);
+    for (int q = 0; q < kLoads; ++q) load_one(q, ks0 + 1);
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
   }
@@ -261,11 +304,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
   auto main_loop = [&](auto energy_tag) {
     constexpr bool kEnergy = decltype(energy_tag)::value;
     u32x4_t ep[2], eq[2];  // energy chunks of even / odd steps
-    if (nfull > 0) {
-      read_step(xa, xb, 0, 0);
-      if (kEnergy) energy_read(ep, 0, 0);
+    if (ks1 > ks0) {
+      read_step(xa, xb, ks0, 0);
+      if (kEnergy) energy_read(ep, ks0, 0);
     }
-    for (int64_t ks = 0; ks < nfull; ++ks) {
+    for (int64_t ks = ks0; ks < ks1; ++ks) {
       // copy c (0..15) of the stage sits in slot 3 (c % 6) of step c / 6
       auto copy = [&](int step, int q) {
         const int c = 6 * step + q / 3;
@@ -312,7 +355,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
   };
   if (diag) main_loop(std::true_type{});
   else main_loop(std::false_type{});
-  if (nfull * kBK < n) {
+  if (has_tail) {
     auto none = [](int) {};
     tail();
 #pragma unroll
@@ -323,6 +366,24 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
       mfma_step(ya, yb, none);
     }
     if (diag) energy_stage(nfull);
+  }
+  if (dst_slot) {
+    // a later part: its sums go to the workspace slot, all 256 x 256 of
+    // them (the folding kernel keeps the upper part inside the matrix)
+    double *eslot = reinterpret_cast<double *>(dst_slot + kTile * kTile);
+    if (diag) eslot[erow] = 2.0 * en;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = wn * 128 + j * 32 + (lane & 31);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          dst_slot[r * kTile + c] = 2.f * acc[i][j][v];
+        }
+      }
+    return;
   }
   if (diag && I0 + erow < d) hdiag[I0 + erow] += 2.0 * en;
 
@@ -352,6 +413,53 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
         if (gr <= gc && gc < d) H[gr * d + gc] = hv[j][v] + 2.f * acc[i][j][v];
       }
     }
+  }
+}
+
+// Adds the workspace slots of the split tiles into H, parts in order (one
+// workgroup per 16-row strip of a tail tile, four columns per thread; a
+// diagonal tile's first strip also adds the parts' energies into hdiag).
+__global__ void __launch_bounds__(256)
+    syrk_fold_kernel(float *__restrict__ H, double *__restrict__ hdiag, int64_t d, int nt,
+                     int ntiles, int parts, int xcd_cus, const float *__restrict__ slots) {
+  const int gi = blockIdx.x >> 4, strip = blockIdx.x & 15;
+  int x = 0, rest = gi;
+  XcdRun run = xcd_run(0, ntiles, xcd_cus);
+  while (rest >= run.tail && x < 7) {
+    rest -= run.tail;
+    run = xcd_run(++x, ntiles, xcd_cus);
+  }
+  int ti, tj;
+  tile_coords(run.first + run.full + rest, nt, ti, tj);
+  const int64_t I0 = int64_t(ti) * kTile, J0 = int64_t(tj) * kTile;
+  const float *s0 = slots + int64_t(gi) * (parts - 1) * kSlotFloats;
+  const bool vec = (d & 3) == 0;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int e = threadIdx.x + 256 * it;      // float4 chunk of the 16 x 256 strip
+    const int r = strip * 16 + (e >> 6), c = (e & 63) * 4;
+    const int64_t gr = I0 + r, gc = J0 + c;
+    if (gr >= d) continue;
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < parts - 1; ++p) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(s0 + p * kSlotFloats + r * kTile + c);
+      if (p == 0) sum = v;
+      else sum += v;
+    }
+    float *h = H + gr * d + gc;
+    if (vec && gr <= gc && gc + 3 < d) {
+      *reinterpret_cast<f32x4_t *>(h) = *reinterpret_cast<const f32x4_t *>(h) + sum;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (gr <= gc + k && gc + k < d) h[k] += sum[k];
+    }
+  }
+  if (ti == tj && strip == 0 && I0 + threadIdx.x < d) {
+    double en = 0.0;
+    for (int p = 0; p < parts - 1; ++p)
+      en += reinterpret_cast<const double *>(s0 + p * kSlotFloats + kTile * kTile)[threadIdx.x];
+    hdiag[I0 + threadIdx.x] += en;
   }
 }
 
@@ -427,18 +535,69 @@ __global__ void __launch_bounds__(256)
 
 }  // namespace
 
+// How the bf16 SYRK's tiles are cut: `parts` token parts per tail tile (1 =
+// no split), chosen to finish the last round soonest with the workspace at
+// hand.  Cost model per XCD, in whole-tile times: full / cus rounds of whole
+// tiles, then ceil(tail parts / cus) rounds of 1/parts of a tile, each
+// round paying a fixed prologue/epilogue of about four 64-token stages.
+struct SyrkPlan {
+  int parts, xcd_cus, units, tail_total;
+};
+
+SyrkPlan plan_syrk(int ntiles, int cus, int64_t n, size_t ws_bytes, int max_parts) {
+  SyrkPlan best{1, std::max(1, cus / 8), 0, 0};
+  const int P = best.xcd_cus;
+  XcdRun runs[8];
+  for (int x = 0; x < 8; ++x) {
+    runs[x] = xcd_run(x, ntiles, P);
+    best.tail_total += runs[x].tail;
+  }
+  const double eps = 4.0 / std::max<int64_t>(n / kBK, 1) + 0.005;
+  double best_score = 1e30;
+  for (int parts = 1; parts <= max_parts; ++parts) {
+    if (parts > 1 && (best.tail_total == 0 ||
+                      size_t(best.tail_total) * (parts - 1) * kSlotBytes > ws_bytes))
+      break;
+    double score = 0.0;
+    int units = 0;
+    for (int x = 0; x < 8; ++x) {
+      const int rounds = (runs[x].tail * parts + P - 1) / P;
+      score = std::max(score, double(runs[x].full) / P * (1.0 + eps) +
+                                  rounds * (1.0 / parts + eps));
+      units = std::max(units, runs[x].full + runs[x].tail * parts);
+    }
+    if (score < best_score - 1e-9) {
+      best_score = score;
+      best.parts = parts;
+      best.units = units;
+    }
+  }
+  return best;
+}
+
+size_t hessian_ws_bytes(int64_t d) {
+  const int nt = (int)cdiv(d, kTile);
+  const SyrkPlan p = plan_syrk(nt * (nt + 1) / 2, device_cu_count(), int64_t(1) << 15,
+                               ~size_t(0), 4);
+  return align256(size_t(p.tail_total) * (p.parts - 1) * kSlotBytes);
+}
+
 gptq_status hessian_accumulate_impl(float *H, double *hdiag, int64_t d, const void *X,
-                                    int x_dtype, int64_t n_tok, int64_t ld_x,
-                                    hipStream_t stream) {
+                                    int x_dtype, int64_t n_tok, int64_t ld_x, void *ws,
+                                    size_t ws_bytes, hipStream_t stream) {
   if (x_dtype == GPTQ_DT_BF16) {
     const uint16_t *Xb = static_cast<const uint16_t *>(X);
     const int nt = (int)cdiv(d, kTile);
     const int ntiles = nt * (nt + 1) / 2;
-    const int per_xcd = (int)cdiv(ntiles, 8);
+    const SyrkPlan p = plan_syrk(ntiles, device_cu_count(), n_tok, ws ? ws_bytes : 0, 16);
+    float *slots = static_cast<float *>(ws);
     const size_t lds = size_t(kStages) * kStageBytes;
     GPTQ_TRY(allow_dynamic_lds((const void *)syrk_bf16_kernel, lds));
-    GPTQ_TRY(launch("hessian_syrk_bf16", syrk_bf16_kernel, dim3(8 * per_xcd), dim3(kThreads), lds,
-                    stream, H, hdiag, Xb, d, n_tok, ld_x, nt, ntiles, per_xcd));
+    GPTQ_TRY(launch("hessian_syrk_bf16", syrk_bf16_kernel, dim3(8 * p.units), dim3(kThreads), lds,
+                    stream, H, hdiag, Xb, d, n_tok, ld_x, nt, ntiles, p.parts, p.xcd_cus, slots));
+    if (p.parts > 1)
+      GPTQ_TRY(launch("hessian_fold", syrk_fold_kernel, dim3(16 * p.tail_total), dim3(256), 0,
+                      stream, H, hdiag, d, nt, ntiles, p.parts, p.xcd_cus, (const float *)slots));
   } else {
     const float *Xf = static_cast<const float *>(X);
     const unsigned nt = (unsigned)cdiv(d, kFT);

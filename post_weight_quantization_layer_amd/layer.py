@@ -56,7 +56,7 @@ class GptqLayer:
 
     def add_batch(self, X: torch.Tensor, stream=None):
         """X: cols x tokens, bfloat16 or float32, on the device."""
-        B.gptq_hessian_accumulate(self.H, self.hdiag, X, stream=stream)
+        B.gptq_hessian_accumulate(self.H, self.hdiag, X, ws=self.ws, stream=stream)
 
     def prepare(self, stream=None):
         B.gptq_prepare_hinv(self.H, self.hdiag, self.params, self.U, self.perm, self.dead,

@@ -60,7 +60,7 @@ def gpu_layer(cfg: I.LayerConfig, W: np.ndarray, chunks, dev="cuda", keep_H=True
                   search=search)
     for xs in chunks:
         t, n, ld = to_device_x(xs, dev)
-        B.gptq_hessian_accumulate(L.H, L.hdiag, t, n_tok=n, ld_x=ld)
+        B.gptq_hessian_accumulate(L.H, L.hdiag, t, n_tok=n, ld_x=ld, ws=L.ws)
         del t
     L.prepare()
     Wd = torch.from_numpy(np.ascontiguousarray(W, dtype=np.float32)).to(dev)

@@ -64,21 +64,24 @@ int main() {
 
   // gptq_hessian_accumulate
   double *dd = static_cast<double *>(fake);
-  expect(gptq_hessian_accumulate(nullptr, dd, 16, fake, GPTQ_DT_BF16, 8, 8, nullptr) ==
-             GPTQ_ERR_INVALID_ARG, "H NULL");
-  expect(gptq_hessian_accumulate(ff, dd, 16, fake, 5, 8, 8, nullptr) == GPTQ_ERR_INVALID_ARG,
-         "x dtype");
-  expect(gptq_hessian_accumulate(ff, dd, 16, fake, GPTQ_DT_BF16, 8, 4, nullptr) ==
+  expect(gptq_hessian_accumulate(nullptr, dd, 16, fake, GPTQ_DT_BF16, 8, 8, nullptr, 0,
+                                 nullptr) == GPTQ_ERR_INVALID_ARG, "H NULL");
+  expect(gptq_hessian_accumulate(ff, dd, 16, fake, 5, 8, 8, nullptr, 0, nullptr) ==
+             GPTQ_ERR_INVALID_ARG, "x dtype");
+  expect(gptq_hessian_accumulate(ff, dd, 16, fake, GPTQ_DT_BF16, 8, 4, nullptr, 0, nullptr) ==
              GPTQ_ERR_INVALID_ARG && said("ld_x"), "ld_x < n");
-  expect(gptq_hessian_accumulate(ff, dd, 16, fake, GPTQ_DT_BF16, 12, 12, nullptr) ==
+  expect(gptq_hessian_accumulate(ff, dd, 16, fake, GPTQ_DT_BF16, 12, 12, nullptr, 0, nullptr) ==
              GPTQ_ERR_INVALID_ARG, "ld_x multiple of 8");
-  expect(gptq_hessian_accumulate(ff, dd, 0, fake, GPTQ_DT_BF16, 8, 8, nullptr) ==
+  expect(gptq_hessian_accumulate(ff, dd, 0, fake, GPTQ_DT_BF16, 8, 8, nullptr, 0, nullptr) ==
              GPTQ_ERR_INVALID_ARG, "d = 0");
   expect(gptq_hessian_accumulate(ff, dd, 16, reinterpret_cast<void *>(uintptr_t(0x10002)),
-                                 GPTQ_DT_BF16, 8, 8, nullptr) == GPTQ_ERR_INVALID_ARG,
+                                 GPTQ_DT_BF16, 8, 8, nullptr, 0, nullptr) == GPTQ_ERR_INVALID_ARG,
          "X misaligned");
-  expect(gptq_hessian_accumulate(ff, dd, 16, nullptr, GPTQ_DT_BF16, 0, 0, nullptr) == GPTQ_OK,
-         "empty chunk");
+  expect(gptq_hessian_accumulate(ff, dd, 16, fake, GPTQ_DT_BF16, 8, 8,
+                                 reinterpret_cast<void *>(uintptr_t(0x10010)), 1 << 20,
+                                 nullptr) == GPTQ_ERR_WORKSPACE, "ws misaligned");
+  expect(gptq_hessian_accumulate(ff, dd, 16, nullptr, GPTQ_DT_BF16, 0, 0, nullptr, 0, nullptr) ==
+             GPTQ_OK, "empty chunk");
 
   // gptq_prepare_hinv workspace
   int32_t *ip = static_cast<int32_t *>(fake);

@@ -71,16 +71,19 @@ def test_quantize_rejects_bad_params(kw, msg):
 
 def test_hessian_rejects_bad_args():
     L = B.lib()
-    assert L.gptq_hessian_accumulate(None, FAKE, 16, FAKE, 1, 8, 8, None) == B.GPTQ_ERR_INVALID_ARG
-    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, FAKE, 5, 8, 8, None) == B.GPTQ_ERR_INVALID_ARG
-    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, FAKE, 1, 8, 4, None) == B.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_hessian_accumulate(None, FAKE, 16, FAKE, 1, 8, 8, None, 0, None) == B.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, FAKE, 5, 8, 8, None, 0, None) == B.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, FAKE, 1, 8, 4, None, 0, None) == B.GPTQ_ERR_INVALID_ARG
     assert "ld_x" in B.gptq_last_error()
-    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, FAKE, 1, 12, 12, None) == B.GPTQ_ERR_INVALID_ARG
-    assert L.gptq_hessian_accumulate(FAKE, FAKE, 0, FAKE, 1, 8, 8, None) == B.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, FAKE, 1, 12, 12, None, 0, None) == B.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_hessian_accumulate(FAKE, FAKE, 0, FAKE, 1, 8, 8, None, 0, None) == B.GPTQ_ERR_INVALID_ARG
     misaligned = ctypes.c_void_p(0x10002)
-    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, misaligned, 1, 8, 8, None) == B.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, misaligned, 1, 8, 8, None, 0, None) == B.GPTQ_ERR_INVALID_ARG
+    # a misaligned workspace
+    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, FAKE, 1, 8, 8, ctypes.c_void_p(0x10010),
+                                     1 << 20, None) == B.GPTQ_ERR_WORKSPACE
     # an empty chunk is a no-op and succeeds without touching anything
-    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, None, 1, 0, 0, None) == B.GPTQ_OK
+    assert L.gptq_hessian_accumulate(FAKE, FAKE, 16, None, 1, 0, 0, None, 0, None) == B.GPTQ_OK
 
 
 def test_prepare_rejects_bad_workspace():
