@@ -55,17 +55,34 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def super_block(cfg):
+    """Columns per lazy super-block of the sweep: the largest multiple m B <= 512
+    of the block B that divides the group size or is a multiple of it (m = 1
+    when B is not a multiple of 4)."""
+    B = cfg.block
+    G = 256 if cfg.grid == "q4k" else cfg.group
+    if B % 4:
+        return B
+    for m in range(512 // B, 1, -1):
+        if G % (m * B) == 0 or (m * B) % G == 0:
+            return m * B
+    return B
+
+
 def kernel_work(cfg, chunk):
     """Algorithmic work of the main kernels.
 
     hessian_syrk_bf16: d(d+1) n_c flops per launch (upper triangle incl.
-    diagonal, 2 per multiply-add).  trailing (the near and far lazy-update
-    GEMMs together): per step, sum over blocks of 2 r B (d - i2) -- the flops
-    of applying every block's errors to every later column."""
-    d, r, B = cfg.cols, cfg.rows, cfg.block
+    diagonal, 2 per multiply-add).  trailing_gemm (the far lazy update, one
+    GEMM per super-block of SB columns): sum over super-blocks of
+    2 r SB (d - s2) flops -- every super-block's errors applied to every
+    later column.  The updates inside a super-block run inside the sweep
+    kernel and are not counted here."""
+    d, r = cfg.cols, cfg.rows
+    sb = super_block(cfg)
     work = {"hessian_syrk_bf16": ("bf16_mfma", d * (d + 1) * chunk)}
-    tr = sum(2 * r * min(B, d - i1) * (d - i1 - min(B, d - i1)) for i1 in range(0, d, B))
-    work["trailing"] = ("f32_mfma", tr)
+    tr = sum(2 * r * min(sb, d - s1) * (d - s1 - min(sb, d - s1)) for s1 in range(0, d, sb))
+    work["trailing_gemm"] = ("f32_mfma", tr)
     return work
 
 
@@ -323,7 +340,7 @@ def main():
         layer.reset_hessian()
         for (a, n) in spans:
             B.gptq_hessian_accumulate(layer.H, layer.hdiag, X[:, a:a + n], n_tok=n,
-                                      ld_x=X.stride(0))
+                                      ld_x=X.stride(0), ws=layer.ws)
         layer.prepare()
         res = layer.quantize(Ws[i], out)
         layer.pack_codes(res.q, packed_q)
@@ -356,7 +373,7 @@ def main():
         B.gptq_profile_enable(False)
 
     kernels = {}
-    names = ["hessian_syrk_bf16", "hessian_syrk_f32", "hessian_diag", "prep_diag",
+    names = ["hessian_syrk_bf16", "hessian_fold", "hessian_syrk_f32", "hessian_diag", "prep_diag",
              "prep_rank_perm", "prep_symmetrize", "prep_gather", "chol_diag_block", "chol_trsm", "chol_near", "chol_syrk",
              "trtri_gemm", "prep_rotate", "quant_gather", "quant_zero_dead", "sweep_affine",
              "sweep_q4k", "trailing_near", "trailing_gemm", "quant_scatter", "quant_g_idx", "pack"]
@@ -369,12 +386,6 @@ def main():
                                 "avg_us": round(tms / n * 1e3, 2)}
     roof = None
     if kernels:
-        # the near and far trailing GEMMs are one step of the method
-        tn = [kernels[k] for k in ("trailing_near", "trailing_gemm") if k in kernels]
-        if tn:
-            ms_t = sum(k["ms_per_step"] for k in tn)
-            kernels["trailing"] = {"launches_per_step": sum(k["launches_per_step"] for k in tn),
-                                   "ms_per_step": round(ms_t, 4)}
         work = kernel_work(cfg, chunk)
         for k, (kind_k, f) in work.items():
             if k not in kernels:

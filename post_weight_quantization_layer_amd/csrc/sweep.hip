@@ -35,11 +35,12 @@ constexpr int kSweepMaxWG = 512;
 struct SweepArgs {
   float *W;        // working weights, row-major, ld = cols (processing order)
   uint8_t *q;      // codes, ld = cols
-  float *Err;      // this block's first column of the error buffer, ld = ldE
+  float *Err;      // the super-block's first column of the error buffer, ld = ldE
   int ldE;
   const float *U;  // ld = cols
   int64_t rows, cols;
-  int i1, B;
+  int s1, B, nblk; // nblk blocks of B columns from column s1 (the last may be shorter)
+  int gblk;        // blocks per group when a group spans several blocks of a launch, else 1
   int bits, group;
   int sub_bits;    // two-level grid: width of the sub-block scale/min codes
   int search;      // affine: importance-weighted grid choice
@@ -168,19 +169,20 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 // kG8: the group size is a multiple of 8, so groups start only at the first
 // column of an 8-column step (the check runs once per 8 columns).
+// One block [i1, i1 + B) of the sweep for all of this workgroup's rows.
 template <int kQ4K, bool kG8>
-__global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
+__device__ __forceinline__ void sweep_block(const SweepArgs &a, const int i1, const int B,
+                                            float *const Err) {
   // LDS: U's block (rows 0 .. Bp+1 of kMaxB floats, Bp = B rounded up to 8,
   // rows and columns past B zero: the fast pass reads two rows ahead), then
   // Bp + 2 reciprocals of the diagonal (zero past B, so padding steps change
   // nothing).
   extern __shared__ __align__(16) float Ub[];
-  const int Bp = (a.B + 7) & ~7;
+  const int Bp = (B + 7) & ~7;
   float *Uinv = Ub + (Bp + 2) * kMaxB;
   // search: the block's column importances (doubles, 8-byte aligned)
   double *hs = reinterpret_cast<double *>(Uinv + ((Bp + 2 + 1) & ~1));
   const int tid = threadIdx.x;
-  const int B = a.B;
   const int64_t ld = a.cols;
   const int lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, sl = lane & 15;
@@ -192,8 +194,8 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
   const int64_t ngroups = a.cols / G;
   const int64_t rows_per_pass = int64_t(gridDim.x) * (kSweepThreads / 64) * 4;
   // 16-byte W accesses need a 4-float aligned row stride and block start
-  const bool vec = (ld & 3) == 0 && (a.i1 & 3) == 0;
-  const bool evec = (a.ldE & 3) == 0 && (reinterpret_cast<uintptr_t>(a.Err) & 15) == 0;
+  const bool vec = (ld & 3) == 0 && (i1 & 3) == 0;
+  const bool evec = (a.ldE & 3) == 0 && (reinterpret_cast<uintptr_t>(Err) & 15) == 0;
   const bool full = vec && c0 + kCPL <= B;  // this lane's 8 columns, 16-byte accesses
 
   // The first row group's weights are requested before the U block, so the
@@ -201,7 +203,7 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
   float w[kCPL];
   auto load_w = [&](int64_t r0) {
     const int64_t rowc = min(r0 + grp, a.rows - 1);
-    const float *wrow = a.W + rowc * ld + a.i1;
+    const float *wrow = a.W + rowc * ld + i1;
     if (full) {
       const f32x4_t t0 = *reinterpret_cast<const f32x4_t *>(wrow + c0);
       const f32x4_t t1 = *reinterpret_cast<const f32x4_t *>(wrow + c0 + 4);
@@ -221,9 +223,9 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
   // U block: rows i1 .. i1+B-1, columns i1 .. i1+B-1, all loads of a thread
   // in one batch before any use; the diagonal's reciprocals from loads of
   // their own.
-  const float *Ublk = a.U + int64_t(a.i1) * ld + a.i1;
+  const float *Ublk = a.U + int64_t(i1) * ld + i1;
   const float udiag = Ublk[int64_t(min(tid, B - 1)) * (ld + 1)];
-  if ((ld & 3) == 0 && (a.i1 & 3) == 0 && (B & 3) == 0) {
+  if ((ld & 3) == 0 && (i1 & 3) == 0 && (B & 3) == 0) {
     constexpr int kPer = kMaxB * kMaxB / 4 / kSweepThreads;  // float4 chunks per thread
     const int nq = B * B / 4;
     f32x4_t v[kPer];
@@ -260,7 +262,7 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
   for (int e = tid; e < (Bp + 2 - B) * kMaxB; e += kSweepThreads) Ub[B * kMaxB + e] = 0.f;
   for (int j = B + tid; j < Bp + 2; j += kSweepThreads) Uinv[j] = 0.f;
   if (a.search)
-    for (int c = tid; c < B; c += kSweepThreads) hs[c] = a.hp[a.i1 + c];
+    for (int c = tid; c < B; c += kSweepThreads) hs[c] = a.hp[i1 + c];
   __syncthreads();
 
   for (; r0 < a.rows; r0 += rows_per_pass) {
@@ -271,14 +273,14 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
     const int64_t row = r0 + grp;
     const bool rv = row < a.rows;  // whole row group is valid or not
     const int64_t rowc = rv ? row : a.rows - 1;
-    float *wrow = a.W + rowc * ld + a.i1;
+    float *wrow = a.W + rowc * ld + i1;
 
     // grid state of the current group (per row group, identical in its lanes)
     float s = 1.f, rs = 1.f, z = 0.f;       // affine
     float Sv = 0.f, Mv = 0.f, rSv = 0.f;    // q4k: sub-lane b < 8 holds S_b, M_b, 1/S_b
 
-    if (a.i1 % G != 0) {  // group began in an earlier block: read its grid back
-      const int64_t gi = a.i1 / G;
+    if (i1 % G != 0) {  // group began in an earlier block: read its grid back
+      const int64_t gi = i1 / G;
       if (!kQ4K) {
         s = a.scale[rowc * ngroups + gi];
         rs = 1.f / s;
@@ -294,11 +296,11 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
     }
 
     // next block column at which a group starts (scalar counter, no division)
-    int jg = (G - a.i1 % G) % G;
+    int jg = (G - i1 % G) % G;
     // choose the grid of the group starting at block column j (from the
     // current, compensated weights)
     auto choose_grid = [&](int j) {
-      const int col = a.i1 + j;
+      const int col = i1 + j;
       const int64_t gi = col / G;
           if (!kQ4K) {
             float mn = INFINITY, mx = -INFINITY;
@@ -350,7 +352,7 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
                   const float v = wrow[c];
                   const float qv = __builtin_amdgcn_fmed3f(rint_div(v, sk, rsk) + z, 0.f, maxq);
                   const float d = __fsub_rn(v, __fmul_rn(sk, qv - z));
-                  e = fma(a.hp[a.i1 + c], double(d) * double(d), e);
+                  e = fma(a.hp[i1 + c], double(d) * double(d), e);
                 }
                 e = group_sum(e);
                 if (e < best) {
@@ -404,7 +406,7 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
                   for (int y = 0; y < kCPL; ++y) {
                     const int p = 128 * t + c0 + y;
                     const float v = (p < B) ? w[y] : wrow[p];
-                    const double hv = (p < B) ? hs[p] : a.hp[a.i1 + p];
+                    const double hv = (p < B) ? hs[p] : a.hp[i1 + p];
                     const float qv =
                         sk > 0.f
                             ? __builtin_amdgcn_fmed3f(rint_div(__fadd_rn(v, mk), sk, rsk), 0.f, maxq)
@@ -465,7 +467,7 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
     float Sl = 0.f, Ml = 0.f, rSl = 0.f;
     auto own_subblock = [&]() {
       if (kQ4K) {
-        const int src = gbase + (((a.i1 & 255) + c0) >> 5);
+        const int src = gbase + (((i1 & 255) + c0) >> 5);
         Sl = shfl(Sv, src);
         Ml = shfl(Mv, src);
         rSl = shfl(rSv, src);
@@ -478,8 +480,8 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
     float wt[kCPL] = {}, qt[kCPL] = {}, et[kCPL] = {};
     auto store_step = [&](int j8) {
       if (!(rv && sl == (j8 >> 3))) return;
-      uint8_t *qrow = a.q + row * ld + a.i1;
-      float *erow = a.Err + row * a.ldE;
+      uint8_t *qrow = a.q + row * ld + i1;
+      float *erow = Err + row * a.ldE;
       if (full && evec) {
         *reinterpret_cast<f32x4_t *>(wrow + c0) = f32x4_t{wt[0], wt[1], wt[2], wt[3]};
         *reinterpret_cast<f32x4_t *>(wrow + c0 + 4) = f32x4_t{wt[4], wt[5], wt[6], wt[7]};
@@ -509,7 +511,7 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
     // the one a step is redone on when its fast pass saw a possible tie.
     auto column_exact = [&](int j8, int x) {
       const int j = j8 + x;
-      const int col = a.i1 + j;
+      const int col = i1 + j;
       const f32x4_t u0 = *reinterpret_cast<const f32x4_t *>(Ub + j * kMaxB + c0);
       const f32x4_t u1 = *reinterpret_cast<const f32x4_t *>(Ub + j * kMaxB + c0 + 4);
       const float uinv = Uinv[j];
@@ -653,6 +655,123 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
       store_step(j8);
     }
     if (r0 + rows_per_pass < a.rows) load_w(r0 + rows_per_pass);
+  }
+}
+
+// The updates a block receives from the earlier blocks of its super-block
+// ("GPTQ", section Komponenty: block updates), applied before its columns
+// are next read: W[rows, i1:i1+B] -= Err[rows, k_lo:k_hi] U[s1+k_lo:s1+k_hi,
+// i1:i1+B] (k counted from the super-block's first column), for this
+// workgroup's 16-row slices of every pass.  The errors are the ones this
+// workgroup wrote while sweeping those blocks, so no other workgroup is
+// involved.  fp32 MFMA 16x16x4: wave w owns block columns [32 w, 32 w + 32)
+// as two 16 x 16 tiles; lane l = 16 g + n feeds A[n][k] = -Err[row n][k]
+// and B[k][n] = U[k][col n] with k = k0 + 4 g + e for MFMA e of a 16-k step
+// (every MFMA sums four k, one per lane group), and holds D[4 g + i][n].
+__device__ __forceinline__ void near_update(const SweepArgs &a, const int i1, const int B,
+                                            const int k_lo, const int k_hi) {
+  constexpr int kC = 32;            // k per chunk: 2 16-k steps
+  constexpr int kQ = kC / 16;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t ld = a.cols;
+  const int64_t rows_per_pass = int64_t(gridDim.x) * (kSweepThreads / 64) * 4;
+  const int K = k_hi - k_lo;
+  // this wave's two 16-column tiles (none past B)
+  const int ntile = min(2, max(0, (B - 32 * wave + 15) / 16));
+  if (ntile == 0) return;   // wave-uniform; the barrier that follows is the caller's
+  int cc[2];
+  bool cok[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int col = 32 * wave + 16 * t + n;
+    cok[t] = t < ntile && col < B;
+    cc[t] = cok[t] ? col : 0;
+  }
+  const float *Ublk = a.U + int64_t(a.s1 + k_lo + 4 * g) * ld + i1;
+  for (int64_t rb = int64_t(blockIdx.x) * 16; rb < a.rows; rb += rows_per_pass) {
+    const int64_t ra = min(rb + n, a.rows - 1);          // this lane's A row
+    const float *er = a.Err + ra * a.ldE + k_lo + 4 * g;
+    f32x4_t acc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = min(rb + 4 * g + i, a.rows - 1);
+        acc[t][i] = a.W[r * ld + i1 + cc[t]];
+      }
+    // a chunk of kC k: Err[ra][k + 4g .. +3] for its 16-k steps q, and
+    // U[k + 4g + x][col] for q, x; fetched one chunk ahead of its MFMAs
+    f32x4_t e[2][kQ];
+    float u[2][2][4 * kQ];
+    auto fetch = [&](int buf, int kc) {
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        const int k = min(kc + 16 * q, K - 16);   // past K: a valid, unused step
+        e[buf][q] = *reinterpret_cast<const f32x4_t *>(er + k);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) u[buf][t][4 * q + x] = Ublk[int64_t(k + x) * ld + cc[t]];
+      }
+    };
+    fetch(0, 0);
+    for (int kc = 0; kc < K; kc += 2 * kC) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int k0 = kc + half * kC;
+        if (k0 >= K) break;
+        if (k0 + kC < K) fetch(half ^ 1, k0 + kC);
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+          if (k0 + 16 * q >= K) break;
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                  -e[half][q][x], cok[t] ? u[half][t][4 * q + x] : 0.f, acc[t], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = rb + 4 * g + i;
+        if (r < a.rows && cok[t]) a.W[r * ld + i1 + cc[t]] = acc[t][i];
+      }
+  }
+}
+
+// A launch sweeps the nblk blocks of one super-block [s1, s1 + nblk B).
+// Before a block is swept it takes the updates of the earlier blocks of the
+// super-block (near_update).  A group is chosen at its first column from
+// all of its columns, so where a group spans gblk > 1 blocks, its later
+// blocks are brought up to date at the group's start and take only the
+// updates of the group's own earlier blocks at their turn.  A workgroup
+// keeps the same rows throughout and reads only the errors it wrote, so
+// the blocks need no synchronization beyond the workgroup's own barriers.
+template <int kQ4K, bool kG8>
+__global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
+  for (int blk = 0; blk < a.nblk; ++blk) {
+    const int i1 = a.s1 + blk * a.B;
+    const int B = min(a.B, int(a.cols - i1));
+    if (blk > 0) {
+      __syncthreads();   // the previous block's LDS reads and its W/Err stores are done
+      const int first = blk - blk % a.gblk;   // first block of this block's group
+      if (blk == first) {
+        for (int b2 = blk; b2 < min(blk + a.gblk, a.nblk); ++b2) {
+          const int j1 = a.s1 + b2 * a.B;
+          near_update(a, j1, min(a.B, int(a.cols - j1)), 0, blk * a.B);
+        }
+      } else {
+        near_update(a, i1, B, first * a.B, blk * a.B);
+      }
+      __syncthreads();   // the updated weights are visible to every wave
+    }
+    sweep_block<kQ4K, kG8>(a, i1, B, a.Err + blk * a.B);
   }
 }
 
@@ -896,12 +1015,18 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   a.sc = sc;
   a.mc = mc;
   // Two-level lazy updates: blocks are grouped into super-blocks of m
-  // blocks.  After each block only the rest of its super-block is updated
-  // (K = B); the columns past the super-block get one update from the whole
-  // super-block's errors (K = m B).  A group's grid is chosen from its
-  // columns' current values, so a group must not reach past its super-block
-  // unless it starts with it: the super-block size divides the group size or
-  // is a multiple of it.
+  // blocks.  Inside a super-block a block's updates reach the super-block's
+  // later blocks (K = B); the columns past the super-block get one update
+  // from the whole super-block's errors (K = m B).  A group's grid is chosen
+  // from its columns' current values, so a group must not reach past its
+  // super-block unless it starts with it: the super-block size divides the
+  // group size or is a multiple of it.
+  //
+  // With B a multiple of 16 a super-block is one launch: each workgroup
+  // applies the updates inside the super-block to its own rows itself
+  // (near_update, fp32 MFMA), from the errors it wrote, just before a block
+  // is swept.  Otherwise every block is a launch of its own, followed by a
+  // GEMM that updates the rest of its super-block.
   const int G = q4k ? 256 : p.group;
   int m = 1;
   if ((B & 3) == 0)
@@ -911,26 +1036,40 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
         break;
       }
   const int SB = m * B;
+  const bool fused = m > 1 && (B % 16) == 0;
   a.ldE = m == 1 ? kMaxB : SB;
+  a.gblk = (fused && G > B && G < SB) ? G / B : 1;
   const char *nm = q4k ? "sweep_q4k" : "sweep_affine";
   const dim3 grid(nwg), blk(kSweepThreads);
+  auto sweep_launch = [&]() -> gptq_status {
+    switch (variant) {
+      case 0: return launch(nm, sweep_kernel<0, false>, grid, blk, lds_launch, stream, a);
+      case 1: return launch(nm, sweep_kernel<0, true>, grid, blk, lds_launch, stream, a);
+      default: return launch(nm, sweep_kernel<1, true>, grid, blk, lds_launch, stream, a);
+    }
+  };
   for (int64_t s1 = 0; s1 < cols; s1 += SB) {
     const int64_t s2 = std::min<int64_t>(s1 + SB, cols);
-    for (int64_t i1 = s1; i1 < s2; i1 += B) {
-      const int Bc = (int)std::min<int64_t>(B, s2 - i1);
-      a.i1 = (int)i1;
-      a.B = Bc;
-      a.Err = Err + (i1 - s1);
-      switch (variant) {
-        case 0: GPTQ_TRY(launch(nm, sweep_kernel<0, false>, grid, blk, lds_launch, stream, a)); break;
-        case 1: GPTQ_TRY(launch(nm, sweep_kernel<0, true>, grid, blk, lds_launch, stream, a)); break;
-        default: GPTQ_TRY(launch(nm, sweep_kernel<1, true>, grid, blk, lds_launch, stream, a)); break;
+    if (fused) {
+      a.s1 = (int)s1;
+      a.B = B;
+      a.nblk = (int)cdiv(s2 - s1, B);
+      a.Err = Err;
+      GPTQ_TRY(sweep_launch());
+    } else {
+      for (int64_t i1 = s1; i1 < s2; i1 += B) {
+        const int Bc = (int)std::min<int64_t>(B, s2 - i1);
+        a.s1 = (int)i1;
+        a.B = Bc;
+        a.nblk = 1;
+        a.Err = Err + (i1 - s1);
+        GPTQ_TRY(sweep_launch());
+        const int64_t i2 = i1 + Bc;
+        if (i2 < s2)
+          GPTQ_TRY(gemm_f32(Err + (i1 - s1), a.ldE, U + i1 * cols + i2, cols, Wp + i2, cols,
+                            (int)rows, (int)(s2 - i2), Bc, -1.f, 1.f, 0, 0, 0, 0, stream,
+                            "trailing_near"));
       }
-      const int64_t i2 = i1 + Bc;
-      if (i2 < s2)
-        GPTQ_TRY(gemm_f32(Err + (i1 - s1), a.ldE, U + i1 * cols + i2, cols, Wp + i2, cols,
-                          (int)rows, (int)(s2 - i2), Bc, -1.f, 1.f, 0, 0, 0, 0, stream,
-                          "trailing_near"));
     }
     if (s2 < cols)
       GPTQ_TRY(gemm_f32(Err, a.ldE, U + s1 * cols + s2, cols, Wp + s2, cols, (int)rows,
