@@ -597,7 +597,7 @@ def quantize_layer(W: np.ndarray, H: np.ndarray, diag: np.ndarray, *, bits: int,
 def reconstruction_error(W: np.ndarray, What: np.ndarray, H: np.ndarray) -> float:
     """||(W - W^) X||_F^2 = 1/2 tr(dW H dW^T) for H = 2 X X^T (undamped)."""
     dW = np.asarray(W, np.float64) - np.asarray(What, np.float64)
-    return 0.5 * float(np.einsum("ij,jk,ik->", dW, H, dW))
+    return 0.5 * float(np.sum((dW @ np.asarray(H, np.float64)) * dW))
 
 
 # --------------------------------------------------------------------------

@@ -6,10 +6,12 @@ tokens (the headline layer), up_proj 28672x8192 (int3), Q4K 14336x4096 --
 the oracle builds the full float64 H (streamed over 8192-token chunks as the
 GPU's inputs are generated) and the full U by the literal route.  The GPU
 must match: H and U within 1e-4 relative (Frobenius), the activation energy
-and the processing order exactly.  32 sampled rows of W are then swept by the
+and the processing order exactly.  128 sampled rows of W are then swept by the
 plain, unblocked oracle (rows are independent given U) and compared code by
 code through the tie-forced replay, grid by grid, and by reconstruction error
-(within 1 %, and below round-to-nearest on the same grid).
+(within 1 %, and below round-to-nearest on the same grid).  The share of
+sampled codes that differ from the plain oracle's is logged and held below
+MAX_RAW_FRAC; the replay requires every one of them to come from a tie.
 """
 import numpy as np
 import pytest
@@ -23,7 +25,15 @@ pytestmark = pytest.mark.gpu
 
 CHUNK = 32768       # tokens per accumulate call (as in the benchmark)
 GEN = 8192          # tokens per host generation step
-NSAMPLE_ROWS = 32
+NSAMPLE_ROWS = 128
+NRTN_ROWS = 32       # of those, rows also rounded to nearest (error comparison)
+# Share of sampled codes that may differ from the plain oracle's.  Every
+# difference must come from a tie (the replay below holds that strictly);
+# a tie's cascade then carries on the order of 1-3 % of the rest of its row,
+# so at 4096-11008 columns about one row in thirty differs in a few hundred
+# codes and the differing share is near 1e-3 for the whole layer -- too near
+# for a fixed sample to hold it below 1e-3 every time.
+MAX_RAW_FRAC = 3e-3
 
 
 def _run_gpu_stream(cfg, on_chunk=None, keep_x=False):
@@ -49,7 +59,7 @@ def _run_gpu_stream(cfg, on_chunk=None, keep_x=False):
             if on_chunk is not None:
                 on_chunk(I.bf16_to_f32(xb))
         B.gptq_hessian_accumulate(L.H, L.hdiag, xall[:, base:base + n], n_tok=n,
-                                  ld_x=xall.stride(0))
+                                  ld_x=xall.stride(0), ws=L.ws)
         log(f"[fullsize] {cfg.name}: accumulated {c0 + n}/{cfg.tokens} tokens")
     L.prepare()
     torch.cuda.synchronize()
@@ -126,8 +136,9 @@ def test_full_size_with_full_oracle(name):
     what[:, perm] = sw.what
     q_gpu = res.q.cpu().numpy()[rows]
     rep = classify_codes(q_gpu[:, perm], sw, cfg.grid, cfg.group)
-    log(f"[fullsize] {name}: codes {rep.mismatches}/{rep.n} differ in {rep.rows_with_mismatch} rows")
-    assert rep.frac <= 1e-3
+    log(f"[fullsize] {name}: codes {rep.mismatches}/{rep.n} differ in {rep.rows_with_mismatch} "
+        f"rows ({rep.frac:.2e})")
+    assert rep.frac <= MAX_RAW_FRAC
     if cfg.grid == "affine":
         grid = {"scale": res.scale.cpu().numpy()[rows], "zero": res.zero.cpu().numpy()[rows]}
     else:
@@ -140,13 +151,16 @@ def test_full_size_with_full_oracle(name):
     w_hat = res.W_hat.cpu().numpy()[rows]
     e_gpu = O.reconstruction_error(Ws, w_hat, H)
     e_or = O.reconstruction_error(Ws, what, H)
-    r = O.rtn(Wp[:, perm], spec)
+    k = NRTN_ROWS
+    r = O.rtn(Wp[:k, perm], spec)
     what_rtn = np.empty_like(r.what)
     what_rtn[:, perm] = r.what
-    e_rtn = O.reconstruction_error(Ws, what_rtn, H)
-    log(f"[fullsize] {name}: E_gpu/E_oracle = {e_gpu / e_or:.6f}, E_gptq/E_rtn = {e_gpu / e_rtn:.4f}")
+    e_rtn = O.reconstruction_error(Ws[:k], what_rtn, H)
+    e_gpu_k = O.reconstruction_error(Ws[:k], w_hat[:k], H)
+    log(f"[fullsize] {name}: E_gpu/E_oracle = {e_gpu / e_or:.6f}, E_gptq/E_rtn = "
+        f"{e_gpu_k / e_rtn:.4f} (first {k} rows)")
     assert abs(e_gpu - e_or) <= 0.01 * e_or
-    assert e_gpu < e_rtn
+    assert e_gpu_k < e_rtn
     # the GPU's weights lie on its own grid (whole layer)
     perm_g = perm
     q_all = res.q.cpu().numpy()
