@@ -55,34 +55,44 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def super_block(cfg):
-    """Columns per lazy super-block of the sweep: the largest multiple m B <= 512
-    of the block B that divides the group size or is a multiple of it (m = 1
-    when B is not a multiple of 4)."""
+def lazy_widths(cfg):
+    """Columns per lazy super-block (SB) and per far group (FG) of the sweep:
+    SB the largest multiple m B <= 512 of the block B, FG the largest
+    multiple of SB <= 2048, each dividing the group size or a multiple of it
+    (SB = B when B is not a multiple of 4)."""
     B = cfg.block
     G = 256 if cfg.grid == "q4k" else cfg.group
-    if B % 4:
-        return B
-    for m in range(512 // B, 1, -1):
-        if G % (m * B) == 0 or (m * B) % G == 0:
-            return m * B
-    return B
+    ok = lambda w: G % w == 0 or w % G == 0
+    sb = B
+    if B % 4 == 0:
+        sb = next((m * B for m in range(512 // B, 1, -1) if ok(m * B)), B)
+    fg = next((c * sb for c in range(2048 // sb, 1, -1) if ok(c * sb)), sb)
+    return sb, fg
 
 
 def kernel_work(cfg, chunk):
     """Algorithmic work of the main kernels.
 
     hessian_syrk_bf16: d(d+1) n_c flops per launch (upper triangle incl.
-    diagonal, 2 per multiply-add).  trailing_gemm (the far lazy update, one
-    GEMM per super-block of SB columns): sum over super-blocks of
-    2 r SB (d - s2) flops -- every super-block's errors applied to every
-    later column.  The updates inside a super-block run inside the sweep
-    kernel and are not counted here."""
+    diagonal, 2 per multiply-add).  The sweep's lazy updates past a
+    super-block of SB columns: trailing_group applies each super-block's
+    errors to the rest of its far group of FG columns (2 r SB (g2 - s2)
+    flops), trailing_gemm each far group's errors to every later column
+    (2 r FG (d - g2)); "trailing" is the two together.  The updates inside
+    a super-block run inside the sweep kernel and are not counted here."""
     d, r = cfg.cols, cfg.rows
-    sb = super_block(cfg)
+    sb, fg = lazy_widths(cfg)
     work = {"hessian_syrk_bf16": ("bf16_mfma", d * (d + 1) * chunk)}
-    tr = sum(2 * r * min(sb, d - s1) * (d - s1 - min(sb, d - s1)) for s1 in range(0, d, sb))
-    work["trailing_gemm"] = ("f32_mfma", tr)
+    tg = tf = 0
+    for g1 in range(0, d, fg):
+        g2 = min(g1 + fg, d)
+        tf += 2 * r * (g2 - g1) * (d - g2)
+        for s1 in range(g1, g2, sb):
+            s2 = min(s1 + sb, g2)
+            tg += 2 * r * (s2 - s1) * (g2 - s2)
+    work["trailing_group"] = ("f32_mfma", tg)
+    work["trailing_gemm"] = ("f32_mfma", tf)
+    work["trailing"] = ("f32_mfma", tg + tf)
     return work
 
 
@@ -376,7 +386,8 @@ def main():
     names = ["hessian_syrk_bf16", "hessian_fold", "hessian_syrk_f32", "hessian_diag", "prep_diag",
              "prep_rank_perm", "prep_symmetrize", "prep_gather", "chol_diag_block", "chol_trsm", "chol_near", "chol_syrk",
              "trtri_gemm", "prep_rotate", "quant_gather", "quant_zero_dead", "sweep_affine",
-             "sweep_q4k", "trailing_near", "trailing_gemm", "quant_scatter", "quant_g_idx", "pack"]
+             "sweep_q4k", "trailing_near", "trailing_group", "trailing_gemm", "quant_scatter",
+             "quant_g_idx", "pack"]
     if not args.no_profile:
         for nme in names:
             n, tms = B.gptq_profile_query(nme)
@@ -386,6 +397,10 @@ def main():
                                 "avg_us": round(tms / n * 1e3, 2)}
     roof = None
     if kernels:
+        tn = [kernels[k] for k in ("trailing_group", "trailing_gemm") if k in kernels]
+        if tn:
+            kernels["trailing"] = {"launches_per_step": sum(k["launches_per_step"] for k in tn),
+                                   "ms_per_step": round(sum(k["ms_per_step"] for k in tn), 4)}
         work = kernel_work(cfg, chunk)
         for k, (kind_k, f) in work.items():
             if k not in kernels:

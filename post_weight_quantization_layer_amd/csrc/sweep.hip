@@ -28,7 +28,8 @@ namespace gptq {
 namespace {
 
 constexpr int kMaxB = 128;
-constexpr int kMaxSuper = 512;      // columns per far (deferred) trailing update
+constexpr int kMaxSuper = 512;      // columns per lazy super-block (one sweep launch)
+constexpr int kMaxGroupCols = 2048; // columns per far-update group of super-blocks
 constexpr int kSweepThreads = 256;  // 4 wavefronts, 4 rows each at a time
 constexpr int kSweepMaxWG = 512;
 
@@ -910,7 +911,7 @@ __global__ void __launch_bounds__(256)
 }  // namespace
 
 size_t quantize_ws_bytes(int64_t rows, int64_t cols, const gptq_params &p) {
-  size_t n = align256(size_t(rows) * kMaxSuper * sizeof(float));  // Err
+  size_t n = align256(size_t(rows) * kMaxGroupCols * sizeof(float));  // Err
   if (p.act_order) {
     n += align256(size_t(rows) * size_t(cols) * sizeof(float));  // Wp
     n += align256(size_t(rows) * size_t(cols));                  // qp
@@ -928,7 +929,7 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   (void)ws_bytes;
   uint8_t *base = static_cast<uint8_t *>(ws);
   float *Err = reinterpret_cast<float *>(base);
-  base += align256(size_t(rows) * kMaxSuper * sizeof(float));
+  base += align256(size_t(rows) * kMaxGroupCols * sizeof(float));
   float *Wp = W;
   uint8_t *qp = q;
   const unsigned gx = (unsigned)std::min<int64_t>(cdiv(cols, 256), 64);
@@ -1014,13 +1015,16 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   a.Dm = Dm;
   a.sc = sc;
   a.mc = mc;
-  // Two-level lazy updates: blocks are grouped into super-blocks of m
-  // blocks.  Inside a super-block a block's updates reach the super-block's
-  // later blocks (K = B); the columns past the super-block get one update
-  // from the whole super-block's errors (K = m B).  A group's grid is chosen
-  // from its columns' current values, so a group must not reach past its
-  // super-block unless it starts with it: the super-block size divides the
-  // group size or is a multiple of it.
+  // Lazy updates on three levels.  Blocks are grouped into super-blocks of
+  // m blocks, and super-blocks into far groups of up to kMaxGroupCols
+  // columns.  Inside a super-block a block's updates reach the super-block's
+  // later blocks (K = B); after a super-block its errors reach the rest of
+  // its far group (K = m B); after a far group, its errors reach every later
+  // column in one product (K = the group's width), the largest and most
+  // efficient GEMM.  The result is that of the unblocked definition ("GPTQ",
+  // section Komponenty: block updates) as long as every column a group's
+  // grid is chosen from is up to date when it is chosen: the super-block
+  // and far-group widths divide the group size or are multiples of it.
   //
   // With B a multiple of 16 a super-block is one launch: each workgroup
   // applies the updates inside the super-block to its own rows itself
@@ -1028,16 +1032,23 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   // is swept.  Otherwise every block is a launch of its own, followed by a
   // GEMM that updates the rest of its super-block.
   const int G = q4k ? 256 : p.group;
+  auto compatible = [&](int w) { return (G % w) == 0 || (w % G) == 0; };
   int m = 1;
   if ((B & 3) == 0)
     for (int c = kMaxSuper / B; c > 1; --c)
-      if ((G % (c * B)) == 0 || ((c * B) % G) == 0) {
+      if (compatible(c * B)) {
         m = c;
         break;
       }
   const int SB = m * B;
+  int FG = SB;   // far-group width: a multiple of SB
+  for (int c = kMaxGroupCols / SB; c > 1; --c)
+    if (compatible(c * SB)) {
+      FG = c * SB;
+      break;
+    }
   const bool fused = m > 1 && (B % 16) == 0;
-  a.ldE = m == 1 ? kMaxB : SB;
+  a.ldE = FG > SB ? FG : (m == 1 ? kMaxB : SB);
   a.gblk = (fused && G > B && G < SB) ? G / B : 1;
   const char *nm = q4k ? "sweep_q4k" : "sweep_affine";
   const dim3 grid(nwg), blk(kSweepThreads);
@@ -1048,32 +1059,40 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
       default: return launch(nm, sweep_kernel<1, true>, grid, blk, lds_launch, stream, a);
     }
   };
-  for (int64_t s1 = 0; s1 < cols; s1 += SB) {
-    const int64_t s2 = std::min<int64_t>(s1 + SB, cols);
-    if (fused) {
-      a.s1 = (int)s1;
-      a.B = B;
-      a.nblk = (int)cdiv(s2 - s1, B);
-      a.Err = Err;
-      GPTQ_TRY(sweep_launch());
-    } else {
-      for (int64_t i1 = s1; i1 < s2; i1 += B) {
-        const int Bc = (int)std::min<int64_t>(B, s2 - i1);
-        a.s1 = (int)i1;
-        a.B = Bc;
-        a.nblk = 1;
-        a.Err = Err + (i1 - s1);
+  for (int64_t g1 = 0; g1 < cols; g1 += FG) {
+    const int64_t g2 = std::min<int64_t>(g1 + FG, cols);
+    for (int64_t s1 = g1; s1 < g2; s1 += SB) {
+      const int64_t s2 = std::min<int64_t>(s1 + SB, g2);
+      float *Es = Err + (s1 - g1);   // this super-block's errors
+      if (fused) {
+        a.s1 = (int)s1;
+        a.B = B;
+        a.nblk = (int)cdiv(s2 - s1, B);
+        a.Err = Es;
         GPTQ_TRY(sweep_launch());
-        const int64_t i2 = i1 + Bc;
-        if (i2 < s2)
-          GPTQ_TRY(gemm_f32(Err + (i1 - s1), a.ldE, U + i1 * cols + i2, cols, Wp + i2, cols,
-                            (int)rows, (int)(s2 - i2), Bc, -1.f, 1.f, 0, 0, 0, 0, stream,
-                            "trailing_near"));
+      } else {
+        for (int64_t i1 = s1; i1 < s2; i1 += B) {
+          const int Bc = (int)std::min<int64_t>(B, s2 - i1);
+          a.s1 = (int)i1;
+          a.B = Bc;
+          a.nblk = 1;
+          a.Err = Es + (i1 - s1);
+          GPTQ_TRY(sweep_launch());
+          const int64_t i2 = i1 + Bc;
+          if (i2 < s2)
+            GPTQ_TRY(gemm_f32(Es + (i1 - s1), a.ldE, U + i1 * cols + i2, cols, Wp + i2, cols,
+                              (int)rows, (int)(s2 - i2), Bc, -1.f, 1.f, 0, 0, 0, 0, stream,
+                              "trailing_near"));
+        }
       }
+      if (s2 < g2)   // the rest of the far group
+        GPTQ_TRY(gemm_f32(Es, a.ldE, U + s1 * cols + s2, cols, Wp + s2, cols, (int)rows,
+                          (int)(g2 - s2), (int)(s2 - s1), -1.f, 1.f, 0, 0, 0, 0, stream,
+                          "trailing_group"));
     }
-    if (s2 < cols)
-      GPTQ_TRY(gemm_f32(Err, a.ldE, U + s1 * cols + s2, cols, Wp + s2, cols, (int)rows,
-                        (int)(cols - s2), (int)(s2 - s1), -1.f, 1.f, 0, 0, 0, 0, stream,
+    if (g2 < cols)   // every later column
+      GPTQ_TRY(gemm_f32(Err, a.ldE, U + g1 * cols + g2, cols, Wp + g2, cols, (int)rows,
+                        (int)(cols - g2), (int)(g2 - g1), -1.f, 1.f, 0, 0, 0, 0, stream,
                         "trailing_gemm"));
   }
 
