@@ -44,8 +44,10 @@ PEAK = {"bf16_mfma": 2500.0, "f32_mfma": 157.3, "hbm": 8000.0}   # TFLOP/s, GB/s
 MEASURED_TRAFFIC = {
     "hessian_syrk_bf16": {
         "source": "post_weight_quantization_layer_amd/csrc/hessian.hip",
-        "sha256": "0111493e8430763706a54d141cce6580c88f3361659ba6275bd1ae13647926d3",
-        "bytes_per_launch": 11898011452,     # 11.90 GB at 32768 tokens per launch
+        "sha256": "26fce1898f91cae22cbad0d01e831f1b58c9622c9cfef8991015e27e7f6276d6",
+        # 12.950 GB fetched + 0.383 GB written at 32768 tokens per launch
+        # (profiles/counters_down_proj_4096x11008_int4_g128.md)
+        "bytes_per_launch": 13332661408,
     },
 }
 CALIB_BYTES = 1 << 30     # the streaming kernel reads and writes this many bytes
