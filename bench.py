@@ -43,11 +43,13 @@ PEAK = {"bf16_mfma": 2500.0, "f32_mfma": 157.3, "hbm": 8000.0}   # TFLOP/s, GB/s
 # the same run.  Reported only while the kernel's source is the one measured.
 MEASURED_TRAFFIC = {
     "hessian_syrk_bf16": {
+        "workload": "down_proj_4096x11008_int4_g128_actorder",
+        "chunk_tokens": 32768,
         "source": "post_weight_quantization_layer_amd/csrc/hessian.hip",
         "sha256": "26fce1898f91cae22cbad0d01e831f1b58c9622c9cfef8991015e27e7f6276d6",
-        # 12.950 GB fetched + 0.383 GB written at 32768 tokens per launch
+        # 13.127 GB fetched + 0.383 GB written at 32768 tokens per launch
         # (profiles/counters_down_proj_4096x11008_int4_g128.md)
-        "bytes_per_launch": 13332661408,
+        "bytes_per_launch": 13510142917,
     },
 }
 CALIB_BYTES = 1 << 30     # the streaming kernel reads and writes this many bytes
@@ -98,9 +100,13 @@ def kernel_work(cfg, chunk):
     return work
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, workload, chunk_tokens):
+    """The counter-measured bytes per launch, for the workload and launch size
+    they were measured on, while the kernel's source is unchanged."""
     m = MEASURED_TRAFFIC.get(kernel)
     if not m or m["sha256"] is None:
+        return None
+    if m["workload"] != workload or m["chunk_tokens"] != chunk_tokens:
         return None
     with open(os.path.join(ROOT, m["source"]), "rb") as f:
         if hashlib.sha256(f.read()).hexdigest() != m["sha256"]:
@@ -417,7 +423,8 @@ def main():
         achieved = per_launch / avg_s / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK[kind], "unit": "TFLOP/s", "frac": round(achieved / PEAK[kind], 4),
-                "traffic": measured_traffic(dom), "algorithmic_flops_per_launch": per_launch}
+                "traffic": measured_traffic(dom, cfg.name, chunk),
+                "algorithmic_flops_per_launch": per_launch}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -11,10 +11,13 @@
 //                   forms e_j = (w_j - q(w_j)) / U_jj and updates the lanes'
 //                   later columns with -e_j U_jk.  Group grids are chosen at a
 //                   group's first column with 16-lane min/max reductions.
-//                   Writes the block's w^ and codes, and e_j into Err.
-//   trailing GEMMs  on fp32 MFMA, in two levels: W[:, i2:s2] -= Err_b U[b, i2:s2]
-//                   within the block's super-block [s1, s2), and once per
-//                   super-block W[:, s2:] -= Err_S U[S, s2:] (K = s2 - s1).
+//                   Writes the block's w^ and codes, and e_j into Err.  One
+//                   launch sweeps a whole super-block of blocks; before each
+//                   block a workgroup applies the earlier blocks' errors to
+//                   its own rows (near_update, fp32 MFMA).
+//   trailing GEMMs  on fp32 MFMA: after a super-block its errors reach the
+//                   rest of its far group, after a far group every later
+//                   column (see the host loop below).
 //
 // Grid decisions (scale, zero, code) are taken in fp32 with IEEE division
 // and round-half-to-even (v_rndne_f32), fp16 super-scales with
