@@ -275,6 +275,13 @@ __global__ void __launch_bounds__(256)
 // The block is padded with an identity to 128 when m < 128.  X (lower) and
 // zeros (upper) are written back over the block.  A pivot that is not > 0
 // and finite sets *flag.
+//
+// Panel solve in the same launch: workgroups 1.. each take 64 rows of the
+// panel below the block (rows k0 + 128 + 64 (b - 1) ..) and overwrite them
+// with L21 = A21 L11^-T.  Every workgroup factors and inverts the block
+// itself (the same instructions on the same data, so the same bits); only
+// workgroup 0 writes the block and the flag.  The rows' loads are issued
+// first and wait in registers while the block is factored.
 constexpr int kDP = 130;            // LDS pitch (floats): conflict-light MFMA reads
 constexpr int kDiagThreads = 256;   // 4 wavefronts
 constexpr size_t kDiagLds = size_t(2) * 128 * kDP * sizeof(float);  // dynamic part
@@ -367,6 +374,20 @@ __global__ void __launch_bounds__(kDiagThreads)
   const float *Ab = A + k0 * d + k0;
   // float4 rows when the block is full and rows are 16-byte aligned
   const bool vec = m == 128 && (d & 3) == 0;
+  // panel rows of this workgroup (blockIdx.x >= 1 only; the launch
+  // guarantees m == 128 and 16-byte aligned rows then): 8 float4 per thread,
+  // piece e = tid + 256 t is row e / 32, columns 4 (e % 32) ..; rows past d
+  // load row d - 1 and are not stored
+  const int64_t pr0 = k0 + 128 + 64 * int64_t(blockIdx.x - 1);
+  f32x4_t pv[8];
+  if (blockIdx.x > 0) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int e = tid + kDiagThreads * t;
+      const int64_t row = min(pr0 + (e >> 5), d - 1);
+      pv[t] = *reinterpret_cast<const f32x4_t *>(A + row * d + k0 + (e & 31) * 4);
+    }
+  }
   if (vec) {
     f32x4_t v[16];
 #pragma unroll
@@ -479,6 +500,34 @@ __global__ void __launch_bounds__(kDiagThreads)
     for_acc(acc2, lane, [&](int r, int c, float v) { X[(64 + 32 * bi + r) * kDP + 32 * bj + c] = -v; });
   }
   __syncthreads();
+  if (blockIdx.x > 0) {
+    // L21 rows = A21 rows x X^T, with the rows staged in L's place:
+    // out[i][j] = sum_k A21[i][k] X[j][k], k <= j (X lower).  Wave w takes
+    // row tile w / 2 and column tiles {0, 3} or {1, 2} (five 32-k blocks
+    // each).
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int e = tid + kDiagThreads * t;
+      float *dst = L + (e >> 5) * kDP + (e & 31) * 4;
+      *reinterpret_cast<float2 *>(dst) = float2{pv[t][0], pv[t][1]};
+      *reinterpret_cast<float2 *>(dst + 2) = float2{pv[t][2], pv[t][3]};
+    }
+    __syncthreads();
+    const int rt = wave >> 1;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int ct = (wave & 1) ? 1 + c : 3 * c;
+      f32x16_t acc = {};
+      for (int kb = 0; kb <= ct; ++kb)
+        mma32<0, 32>(acc, lane, [&](int mm, int k) { return L[(32 * rt + mm) * kDP + 32 * kb + k]; },
+                     [&](int k, int n) { return X[(32 * ct + n) * kDP + 32 * kb + k]; });
+      for_acc(acc, lane, [&](int r, int cc, float v) {
+        const int64_t row = pr0 + 32 * rt + r;
+        if (row < d) A[row * d + k0 + 32 * ct + cc] = v;
+      });
+    }
+    return;
+  }
   if (tid == 0 && bad) *flag = 1;
   float *Aw = A + k0 * d + k0;
   if (vec) {
@@ -591,6 +640,7 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
   // ---- blocked Cholesky A = L L^T; diagonal blocks end up holding L_ii^-1
   const size_t lds = kDiagLds;
   GPTQ_TRY(allow_dynamic_lds((const void *)potrf_inv_block_kernel, lds));
+  const int cus = device_cu_count();
   // Two levels: the trailing update inside a panel of kPanel columns is
   // applied after each diagonal block (K = 128), the update of the columns
   // past the panel once per panel (K = kPanel).
@@ -598,14 +648,22 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
     const int64_t c1 = std::min<int64_t>(c0 + kPanel, d);
     for (int64_t k0 = c0; k0 < c1; k0 += kNB) {
       const int m = (int)std::min<int64_t>(kNB, d - k0);
-      GPTQ_TRY(launch("chol_diag_block", potrf_inv_block_kernel, dim3(1), dim3(kDiagThreads), lds,
-                      stream, A, d, k0, m, flag));
       const int64_t r = d - k0 - m;
+      // The panel below the block is solved in the same launch when its
+      // 64-row slices, plus the block's own workgroup, fit in one round of
+      // the chip (every workgroup factors the block; a second round would
+      // repeat that on the critical path).
+      const int64_t slices = r > 0 ? cdiv(r, 64) : 0;
+      const bool fused = slices > 0 && (d & 3) == 0 && 1 + slices <= cus;
+      GPTQ_TRY(launch("chol_diag_block", potrf_inv_block_kernel,
+                      dim3(unsigned(fused ? 1 + slices : 1)), dim3(kDiagThreads), lds, stream, A,
+                      d, k0, m, flag));
       if (r <= 0) break;
       float *A21 = A + (k0 + m) * d + k0;
       // L21 = A21 * L11^-T   (in place: each workgroup owns whole rows)
-      GPTQ_TRY(gemm_f32(A21, d, A + k0 * d + k0, d, A21, d, (int)r, m, m, 1.f, 0.f, 1, 0, 0, 0,
-                        stream, "chol_trsm"));
+      if (!fused)
+        GPTQ_TRY(gemm_f32(A21, d, A + k0 * d + k0, d, A21, d, (int)r, m, m, 1.f, 0.f, 1, 0, 0, 0,
+                          stream, "chol_trsm"));
       // the rest of the panel: A[k0+m:, k0+m:c1] -= L21 L21[0:c1-k0-m]^T
       // (the part of it above the diagonal is written too, and never read)
       const int64_t nn = c1 - (k0 + m);
