@@ -125,6 +125,25 @@ def test_odd_width_small_groups(act):
     assert abs(e_gpu - e_or) <= 0.01 * e_or
 
 
+@pytest.mark.parametrize("cols,act", [(1000, True), (1096, False)])
+def test_width_not_a_multiple_of_the_block(cols, act):
+    """A width that is a multiple of 4 but not of 128: the inverse factor's
+    last diagonal block is partial (1000 = 7 x 128 + 104) and the panel rows
+    below a block end in a partial 64-row slice (1096 = 8 x 128 + 72); the
+    Hessian's last 256-wide tiles are ragged too."""
+    cfg = I.CONFIGS["q_proj_4096x4096_int4_g128"].with_(rows=40, cols=cols, tokens=900, group=8,
+                                                       block=8, act_order=act)
+    W = I.weight(cfg)
+    store = [I.x_chunk_storage(cfg, 0, 900)]
+    g = gpu_layer(cfg, W, store)
+    o, H, diag = oracle_layer(cfg, W.astype(np.float64), [I.bf16_to_f32(store[0])])
+    assert rel_fro(g.U, o.U) <= 1e-4
+    check_replay(cfg, W, o, g, tag=f"cols={cols} act={act}")
+    e_gpu = O.reconstruction_error(W, g.W_hat, H)
+    e_or = O.reconstruction_error(W, o.what, H)
+    assert abs(e_gpu - e_or) <= 0.01 * e_or
+
+
 @pytest.mark.parametrize("bits,group,block", [(2, 64, 64), (8, 128, 128), (3, 512, 128),
                                               (5, 32, 128)])
 def test_bit_widths_and_per_channel(bits, group, block):
