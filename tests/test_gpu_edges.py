@@ -125,6 +125,40 @@ def test_odd_width_small_groups(act):
     assert abs(e_gpu - e_or) <= 0.01 * e_or
 
 
+@pytest.mark.parametrize("d", [1152, 4096])
+def test_hessian_with_and_without_workspace(d):
+    """The SYRK's last round split over token ranges (workspace given, also a
+    workspace too small for every part) and unsplit (no workspace): each
+    within the bar of the float64 H and energy, and bitwise repeatable."""
+    import torch
+    from post_weight_quantization_layer_amd import binding as B
+    from tests.gpu_harness import to_device_x
+    cfg = I.CONFIGS["q_proj_4096x4096_int4_g128"].with_(rows=8, cols=d, tokens=2500)
+    xs = I.x_chunk_storage(cfg, 0, 2500)
+    t, n, ld = to_device_x(xs, "cuda")
+    H64 = O.hessian([I.bf16_to_f32(xs)])
+    diag64 = O.hessian_diag([I.bf16_to_f32(xs)])
+    iu = np.triu_indices(d)
+    full = B.gptq_workspace_bytes(8, d, B.make_params(4, 128, 128, False, 0.01, "affine", False))
+    for name, nbytes in (("none", 0), ("small", 256 * 256 * 4 + 2048), ("full", full)):
+        outs = []
+        for _ in range(2):
+            H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+            hd = torch.zeros(d, dtype=torch.float64, device="cuda")
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
+            B.gptq_hessian_accumulate(H, hd, t, n_tok=n, ld_x=ld, ws=ws)
+            torch.cuda.synchronize()
+            outs.append((H.cpu().numpy(), hd.cpu().numpy()))
+        np.testing.assert_array_equal(outs[0][0], outs[1][0], err_msg=f"{name}: H not repeatable")
+        Hg, hdg = outs[0]
+        err = rel_fro(Hg[iu], H64[iu])
+        log(f"[hessian ws] d={d} {name}: rel err {err:.2e}")
+        assert err <= 1e-4
+        assert np.all(np.tril(Hg, -1) == 0)
+        np.testing.assert_array_equal(outs[0][1], outs[1][1], err_msg=f"{name}: energy not repeatable")
+        assert rel_fro(hdg, diag64) <= 1e-12
+
+
 @pytest.mark.parametrize("cols,act", [(1000, True), (1096, False)])
 def test_width_not_a_multiple_of_the_block(cols, act):
     """A width that is a multiple of 4 but not of 128: the inverse factor's
