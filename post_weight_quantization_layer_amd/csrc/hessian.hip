@@ -1,8 +1,10 @@
 // Hessian accumulation H += 2 X X^T ("GPTQ", section Komponenty) and the
 // float64 activation energy hdiag += 2 sum_t x_it^2.
 //
-// bf16 path: a SYRK on bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 accumulate.
-// Only the upper-triangle 256x256 tiles of H are computed.  Most tiles are
+// bf16 path: a SYRK on bf16 MFMA, fp32 accumulate.  Only the upper-triangle
+// 256x256 tiles of H are computed: diagonal tiles on v_mfma_f32_32x32x16_bf16
+// (with the energy), the others on v_mfma_f32_16x16x32_bf16, which holds a
+// higher shader clock on gfx950 for the same work.  Most tiles are
 // owned by one workgroup that runs the whole token loop, so H is updated by
 // one read-modify-write per tile.  The tiles of the last, partly filled
 // round may instead be split into `parts` token ranges run by different
@@ -137,6 +139,214 @@ __host__ __device__ inline XcdRun xcd_run(int x, int ntiles, int cus) {
 constexpr int64_t kSlotFloats = int64_t(kTile) * kTile + 2 * kTile;
 constexpr size_t kSlotBytes = size_t(kSlotFloats) * sizeof(float);
 
+// ---- Off-diagonal tiles: 16x16x32 bf16 MFMAs, no energy.  On gfx950 this
+// MFMA shape runs at a higher shader clock than 32x32x16 for the same work
+// (1.74 against 1.52 GHz in this kernel).  Same LDS ring as the diagonal-tile
+// path (two 64-token stages of 128-byte rows, same swizzle, conflict-free
+// for the 16-row fragment reads by the bank-conflict counter); each stage
+// is two 32-token steps.
+
+// One off-diagonal tile (every entry above the diagonal): each wave owns a
+// 128 x 128 sub-tile as 8 x 8 blocks of 16 x 16.  Iteration ks: step 0
+// multiplies the first 32 tokens of stage ks with fragment set X while set Y
+// (the second 32 tokens) is read, and stores stage ks+1 (loaded one
+// iteration earlier) to the ring slot of stage ks-1, re-issuing each
+// register's load for stage ks+2; a barrier makes stage ks+1 visible; step 1
+// multiplies set Y while set X is read from stage ks+1.  Every read of a ring
+// slot precedes the barrier after which that slot is rewritten.  The ragged
+// token tail is one more stage whose loads come from clamped addresses and
+// whose tokens at or past n are zeroed before they are stored.
+__device__ __forceinline__ void syrk_tile16(float *__restrict__ H, const uint16_t *__restrict__ X,
+                                            int64_t d, int64_t n, int64_t ld, int64_t I0,
+                                            int64_t J0, int part, int nparts,
+                                            float *__restrict__ dst_slot, uint8_t *smem,
+                                            int tid) {
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x4_t acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Stages of this unit: the ragged token tail first (last part only; its
+  // loads are masked), then whole 64-token stages.  Every unit has at least
+  // one whole stage (the host checks it), so the loop below only ever
+  // touches whole stages.
+  const int64_t nfull = n / kBK;
+  const int64_t ks0 = nfull * part / nparts;
+  const int r = (part == nparts - 1 && nfull * kBK < n) ? 1 : 0;
+  const int U = (int)(nfull * (part + 1) / nparts - ks0) + r;
+  auto stage_k = [&](int t) {   // first token of stage t (past the last: the last)
+    t = min(t, U - 1);
+    return t < r ? nfull * kBK : (ks0 + t - r) * kBK;
+  };
+
+  // Load q of a lane: row tid/8 + 32 (q%8) of panel q/8 at 16-byte chunk
+  // tid%8 (eight lanes read one row's 128 contiguous bytes).  The address is
+  // a uniform base (the group's first row, clamped, at the stage's first
+  // token) plus a per-lane 32-bit byte offset fixed for the whole loop, so a
+  // load costs no vector ALU work.  Rows past d are clamped to row d-1.  The
+  // ragged last stage takes the general per-lane path: a chunk wholly past n
+  // reads the row's first chunk instead (zeroed when stored).
+  const int lrow = tid >> 3, lchunk = tid & 7;
+  const int lds_off = lrow * kRowBytes + ((lchunk ^ swz(lrow)) << 4);
+  int64_t grow[kLoads];
+  uint32_t voff[kLoads];
+#pragma unroll
+  for (int q = 0; q < kLoads; ++q) {
+    const int64_t r0 = (q < kPanelLoads ? I0 : J0) + 32 * (q % kPanelLoads);
+    grow[q] = min(r0, d - 1);
+    voff[q] = uint32_t((min(r0 + lrow, d - 1) - grow[q]) * ld * 2 + lchunk * 16);
+  }
+  u32x4_t stg[kLoads];
+  // Whole stage: a uniform base plus the lane's fixed offset, no vector ALU
+  // work.  General form (the ragged stage, outside the loop): a chunk wholly
+  // past n reads the row's first chunk instead, and at the store the tokens
+  // at or past n become 0 (a chunk that holds n lies inside the row's
+  // storage: ld is a multiple of 8 and at least n).
+  auto load_one = [&](int q, int t) {
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(X + grow[q] * ld + stage_k(t));
+    stg[q] = *reinterpret_cast<const u32x4_t *>(base + voff[q]);
+  };
+  auto load_any = [&](int q, int t) {
+    const int64_t k = stage_k(t);
+    const uint16_t *p = X + grow[q] * ld + voff[q] / 2;
+    stg[q] = *reinterpret_cast<const u32x4_t *>(p + (k + lchunk * 8 < n ? k : 0));
+  };
+  auto store_one = [&](int q, int t) {
+    *reinterpret_cast<u32x4_t *>(smem + (t & 1) * kStageBytes + lds_off +
+                                 (q / kPanelLoads) * kPanelBytes +
+                                 (q % kPanelLoads) * 32 * kRowBytes) = stg[q];
+  };
+  auto store_any = [&](int q, int t) {
+    const int64_t valid = n - (stage_k(t) + lchunk * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      stg[q][w] &= (2 * w < valid ? 0xffffu : 0u) | (2 * w + 1 < valid ? 0xffff0000u : 0u);
+    store_one(q, t);
+  };
+  // Set X (step 0): the B fragments and a ring of four A fragments (block
+  // row i in slot i % 4), rows 0-2 read during the previous step 1, rows
+  // 3-7 three block rows ahead inside step 0 (before the barrier that lets
+  // their ring slot be rewritten).  Set Y (step 1, after that barrier) is
+  // read whole during step 0.
+  bf16x8_t xa[4], xb[8], ya[8], yb[8];
+  auto frag_a = [&](int u, int h, int i) {
+    return read_frag(smem + (u & 1) * kStageBytes, wm * 128 + 16 * i + (lane & 15),
+                     4 * h + (lane >> 4));
+  };
+  auto frag_b = [&](int u, int h, int j) {
+    return read_frag(smem + (u & 1) * kStageBytes + kPanelBytes, wn * 128 + 16 * j + (lane & 15),
+                     4 * h + (lane >> 4));
+  };
+  // Copies: registers 8-15 carry stage u+1 into step 0 of iteration u (then
+  // load stage u+2), registers 0-7 carry stage u+2 into step 1 of iteration
+  // u (then load stage u+3).  Both land in a ring slot whose last reads came
+  // before the previous barrier.
+  if (U > 0) {
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) load_any(q, 0);
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) store_any(q, 0);
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) load_any(q, 1);
+#pragma unroll
+    for (int q = 0; q < kLoads / 2; ++q) {
+      store_any(q, 1);
+      load_any(q, 2);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xb[j] = frag_b(0, 0, j);
+    xa[0] = frag_a(0, 0, 0);
+    xa[1] = frag_a(0, 0, 1);
+    xa[2] = frag_a(0, 0, 2);
+  }
+  for (int u = 0; u < U; ++u) {
+    // step 0, slot 8i+j: A row i+3 after (i, 1); set Y fragment f (a0 b0 ..
+    // b7 a1 .. a7) in slot 4f+2; copy 8+i in slot 8i+5.
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i % 4], xb[j], acc[i][j], 0, 0, 0);
+        const int q = 8 * i + j;
+        if (j == 1 && i + 3 < 8) xa[(i + 3) % 4] = frag_a(u, 0, i + 3);
+        if ((q & 3) == 2) {
+          const int f = q >> 2;
+          if (f == 0) ya[0] = frag_a(u, 1, 0);
+          else if (f < 9) yb[f - 1] = frag_b(u, 1, f - 1);
+          else ya[f - 8] = frag_a(u, 1, f - 8);
+        }
+        if (j == 5) {
+          store_one(kLoads / 2 + i, u + 1);
+          load_one(kLoads / 2 + i, u + 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): stores of u+1, reads of u done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1: set X of the next stage (past the last stage: unused), B
+    // fragment i after (i, 2), A rows 0-2 after (i, 6); copy i in slot 8i+5.
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya[i], yb[j], acc[i][j], 0, 0, 0);
+        if (j == 2) xb[i] = frag_b(u + 1, 0, i);
+        if (i < 3 && j == 6) xa[i] = frag_a(u + 1, 0, i);
+        if (j == 5) {
+          store_one(i, u + 2);
+          load_one(i, u + 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+  // 16x16 MFMA result layout: lane l, element v -> row 4*(l/16) + v, col l%16.
+  if (dst_slot) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = wn * 128 + 16 * j + (lane & 15);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = wm * 128 + 16 * i + 4 * (lane >> 4) + v;
+          dst_slot[r * kTile + c] = 2.f * acc[i][j][v];
+        }
+      }
+    return;
+  }
+  // H += 2 * acc inside the matrix (every entry of this tile is above the
+  // diagonal).  One block row (32 values per lane) at a time: its loads are
+  // issued from clamped (valid) addresses before any store.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float hv[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t gc = min(J0 + wn * 128 + 16 * j + (lane & 15), d - 1);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t gr = min(I0 + wm * 128 + 16 * i + 4 * (lane >> 4) + v, d - 1);
+        hv[j][v] = H[gr * d + gc];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t gc = J0 + wn * 128 + 16 * j + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t gr = I0 + wm * 128 + 16 * i + 4 * (lane >> 4) + v;
+        if (gr < d && gc < d) H[gr * d + gc] = hv[j][v] + 2.f * acc[i][j][v];
+      }
+    }
+  }
+}
+
 // One workgroup per CU (128 KB of LDS) and one wave per SIMD: the kernel may
 // use the whole register file, so both fragment sets stay in registers.
 // Workgroup (xcd, slot): slot < full -> whole tile first + slot; else unit
@@ -146,7 +356,8 @@ constexpr size_t kSlotBytes = size_t(kSlotFloats) * sizeof(float);
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
     syrk_bf16_kernel(float *__restrict__ H, double *__restrict__ hdiag,
                      const uint16_t *__restrict__ X, int64_t d, int64_t n, int64_t ld, int nt,
-                     int ntiles, int parts, int xcd_cus, float *__restrict__ slots) {
+                     int ntiles, int parts, int xcd_cus, float *__restrict__ slots,
+                     int tile16) {
   const int bid = blockIdx.x;
   const int xcd = bid & 7, slot = bid >> 3;
   const XcdRun run = xcd_run(xcd, ntiles, xcd_cus);
@@ -173,6 +384,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
 
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x;
+  if (!diag && tile16) {
+    syrk_tile16(H, X, d, n, ld, I0, J0, part, nparts, dst_slot, smem, tid);
+    return;
+  }
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;  // sub-tile rows wm*128.., cols wn*128..
@@ -593,8 +808,12 @@ gptq_status hessian_accumulate_impl(float *H, double *hdiag, int64_t d, const vo
     float *slots = static_cast<float *>(ws);
     const size_t lds = size_t(kStages) * kStageBytes;
     GPTQ_TRY(allow_dynamic_lds((const void *)syrk_bf16_kernel, lds));
+    // Off-diagonal tiles take the 16x16x32 path when every token part holds a
+    // whole 64-token stage and the per-lane row offsets fit in 32 bits.
+    const int tile16 = (n_tok / kBK >= p.parts && ld_x < (int64_t(1) << 26)) ? 1 : 0;
     GPTQ_TRY(launch("hessian_syrk_bf16", syrk_bf16_kernel, dim3(8 * p.units), dim3(kThreads), lds,
-                    stream, H, hdiag, Xb, d, n_tok, ld_x, nt, ntiles, p.parts, p.xcd_cus, slots));
+                    stream, H, hdiag, Xb, d, n_tok, ld_x, nt, ntiles, p.parts, p.xcd_cus, slots,
+                    tile16));
     if (p.parts > 1)
       GPTQ_TRY(launch("hessian_fold", syrk_fold_kernel, dim3(16 * p.tail_total), dim3(256), 0,
                       stream, H, hdiag, d, nt, ntiles, p.parts, p.xcd_cus, (const float *)slots));
