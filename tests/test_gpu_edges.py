@@ -159,6 +159,39 @@ def test_hessian_with_and_without_workspace(d):
         assert rel_fro(hdg, diag64) <= 1e-12
 
 
+@pytest.mark.parametrize("n", [1, 40, 63, 64, 100, 197, 4097])
+def test_hessian_token_counts(n):
+    """Token counts around the SYRK's 64-token stage, with and without the
+    split workspace: off-diagonal tiles take the 16x16x32 path when every
+    token part holds a whole stage (its ragged stage loaded first, masked)
+    and the 32x32x16 path otherwise; d = 520 has three tile rows, the last
+    ragged.  H and the energy within the bar of the float64 ones."""
+    import torch
+    from post_weight_quantization_layer_amd import binding as B
+    from tests.gpu_harness import to_device_x
+    d = 520
+    cfg = I.CONFIGS["q_proj_4096x4096_int4_g128"].with_(rows=8, cols=d, tokens=n)
+    xs = I.x_chunk_storage(cfg, 0, n)
+    t, nn, ld = to_device_x(xs, "cuda")
+    t[:, nn:] = 100.0   # the row padding must never be read as tokens
+    H64 = O.hessian([I.bf16_to_f32(xs)])
+    diag64 = O.hessian_diag([I.bf16_to_f32(xs)])
+    iu = np.triu_indices(d)
+    full = B.gptq_workspace_bytes(8, d, B.make_params(4, 8, 8, False, 0.01, "affine", False))
+    for name, nbytes in (("none", 0), ("full", full)):
+        H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+        hd = torch.zeros(d, dtype=torch.float64, device="cuda")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
+        B.gptq_hessian_accumulate(H, hd, t, n_tok=nn, ld_x=ld, ws=ws)
+        torch.cuda.synchronize()
+        Hg, hdg = H.cpu().numpy(), hd.cpu().numpy()
+        err = rel_fro(Hg[iu], H64[iu])
+        log(f"[hessian n] n={n} {name}: rel err {err:.2e}")
+        assert err <= 1e-4
+        assert np.all(np.tril(Hg, -1) == 0)
+        assert rel_fro(hdg, diag64) <= 1e-12
+
+
 @pytest.mark.parametrize("cols,act", [(1000, True), (1096, False)])
 def test_width_not_a_multiple_of_the_block(cols, act):
     """A width that is a multiple of 4 but not of 128: the inverse factor's
