@@ -437,6 +437,184 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(W4Args a) {
 }
 
 
+// The same product for splits of many chunks: two chunks of x in LDS and two
+// sets of weights in registers.  While chunk c is multiplied, chunk c+1's x
+// waits in registers (loaded during chunk c-1) and goes to the other LDS
+// buffer after the multiplication; then chunk c+2's x is loaded and its
+// weights are issued into the set just freed.  ns_max is a power of two, at
+// most 4 steps (2 from three 16-row slabs of x up), so that two workgroups
+// fit a CU.
+template <int MT, int SPS, int NS>
+__global__ __launch_bounds__(kThreads) void w4a16_gemm_pipe_kernel(W4Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int kSub = 4 / SPS;  // sub-steps per scale unit
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+  const int tile = blockIdx.x / a.splits, split = blockIdx.x - tile * a.splits;
+  const int kbeg = split * a.base + min(split, a.rem);  // this split's steps:
+  const int nsplit = a.base + (split < a.rem ? 1 : 0);  //   [kbeg, kbeg + nsplit)
+  const int rt0 = (tile * kWaves + wave) * kNT;
+  const int row_h = a.ns_max * kStep + 8;  // LDS row stride in halves (+16 B)
+  const int buf_h = 16 * MT * row_h;        // halves per staged chunk of x
+  uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
+
+  u4_t wb[2][NS][kNT];
+  float sb[2][NS][kNT][SPS];
+  uint32_t zb[2][NS][kNT][SPS];
+  auto issue = [&](int set, int slot, int st) {
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) {
+      const int64_t rt = min(rt0 + j, a.rt16 - 1);
+      wb[set][slot][j] = a.wq[(rt * a.ksteps + st) * 64 + lane];
+#pragma unroll
+      for (int u = 0; u < SPS; ++u) {
+        const int64_t g = SPS == 1 ? st / a.gsteps : int64_t(st) * SPS + u;
+        sb[set][slot][j][u] = a.sc[(rt * a.ngp + g) * 16 + n];
+        zb[set][slot][j][u] = a.zp[(rt * a.ngp + g) * 2 + (n >> 3)];
+      }
+    }
+  };
+
+  f4_t yacc[MT][kNT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) yacc[m][j] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  const DqConst dq = dq_const();
+
+  // This thread's 16-byte pieces of a staged chunk of x: piece i is row
+  // b0 + i db, piece c0 of the row's cpr = 16 ns_max pieces (ns_max is a
+  // power of two, so cpr divides the 256 threads).
+  constexpr int kChunks = MT * NS;   // >= 16 MT rows x cpr pieces / 256 threads
+  const int cpr = a.ns_max * (kStep / 8);
+  const int lg = __builtin_ctz(cpr);
+  const int b0 = tid >> lg, c0 = tid & (cpr - 1), db = kThreads >> lg;
+  // Chunk c of the split: steps [kbeg + c ns_max, ...) (rows >= batch and
+  // columns >= cols are zero; a chunk past the split loads nothing).
+  const int nchunks = (nsplit + a.ns_max - 1) / a.ns_max;
+  u4_t stg[kChunks];
+  auto x_load = [&](int c) {
+    const int col = (kbeg + c * a.ns_max) * kStep + c0 * 8;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int b = b0 + i * db;
+      stg[i] = u4_t{0, 0, 0, 0};
+      if (c < nchunks && b < a.batch && col < a.cols)
+        stg[i] = *reinterpret_cast<const u4_t *>(a.x + b * a.ldx + col);
+    }
+  };
+  auto x_store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int b = b0 + i * db;
+      if (b < 16 * MT) *reinterpret_cast<u4_t *>(xs + buf * buf_h + b * row_h + c0 * 8) = stg[i];
+    }
+  };
+  // the weights of chunk c (slots past its steps repeat its last step, or the
+  // split's last step past the split: same cache lines)
+  auto w_issue = [&](int set, int c) {
+    const int k0 = kbeg + c * a.ns_max;
+    const int last = kbeg + nsplit - 1;
+#pragma unroll
+    for (int p = 0; p < NS; ++p) issue(set, p, min(k0 + min(p, a.ns_max - 1), last));
+  };
+
+  // One step of chunk buffer `buf` with weight set `set`: 4 MFMA sub-steps
+  // per slab and tile; the scale of each unit is applied to its fp32 sum.
+  auto step = [&](auto settag, int buf, const int p) {
+    constexpr int set = decltype(settag)::value;
+    const uint16_t *xa = xs + buf * buf_h + n * row_h + 8 * kg;  // lane's A row and k offset
+    f4_t acc[MT][kNT];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      h8_t A[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        A[m] = *reinterpret_cast<const h8_t *>(xa + m * 16 * row_h + p * kStep + 32 * t);
+      const int u = t / kSub;
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) {
+        const uint32_t z = (zb[set][p][j][u] >> (4 * (n & 7))) & 15u;
+        const uint32_t nz1 = (0xE400u | z) * 0x00010001u;
+        const uint32_t nz2 = (0xD400u | (z << 4)) * 0x00010001u;
+        const h8_t B = dequant8(wb[set][p][j][t], nz1, nz2, dq);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const f4_t c0 = (t % kSub == 0) ? f4_t{0.f, 0.f, 0.f, 0.f} : acc[m][j];
+          acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[m], B, c0, 0, 0, 0);
+        }
+        if (t % kSub == kSub - 1) {
+          const float sc = sb[set][p][j][u];
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) yacc[m][j][i] = fmaf(sc, acc[m][j][i], yacc[m][j][i]);
+        }
+      }
+    }
+  };
+  // Chunk c: multiply buffer c % 2 with weight set c % 2; meanwhile chunk
+  // c+1's x waits in registers (loaded during chunk c-1) and is stored to
+  // the other buffer after the multiplication, chunk c+2's x is loaded and
+  // its weights are issued into the freed set.  The barrier at the end of a
+  // chunk orders the other buffer's stores before its reads, and this
+  // buffer's reads before its next stores.
+  auto chunk = [&](auto settag, int c) {
+    constexpr int set = decltype(settag)::value;
+    const int ns = min(a.ns_max, nsplit - c * a.ns_max);
+#pragma unroll
+    for (int p = 0; p < NS; ++p)
+      if (p < ns) step(settag, set, p);
+    x_store(set ^ 1);
+    x_load(c + 2);
+    w_issue(set, c + 2);
+    __syncthreads();
+  };
+  x_load(0);
+  w_issue(0, 0);
+  x_store(0);
+  x_load(1);
+  w_issue(1, 1);
+  __syncthreads();
+  for (int c = 0; c < nchunks; c += 2) {
+    chunk(std::integral_constant<int, 0>{}, c);
+    if (c + 1 < nchunks) chunk(std::integral_constant<int, 1>{}, c + 1);
+  }
+
+  // ---- output.  Lane holds C[m = 4 kg + i][n] of each 16 x 16 block.
+  if (a.splits == 1) {
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) {
+      const int r = (rt0 + j) * 16 + n;
+      if (rt0 + j >= a.rt16 || r >= a.rows) continue;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int b = m * 16 + 4 * kg + i;
+          if (b < a.batch)
+            a.y[b * a.ldy + r] = __builtin_bit_cast(uint16_t, _Float16(yacc[m][j][i]));
+        }
+    }
+    return;
+  }
+  float *mine = a.part + int64_t(split) * a.batch * a.rows_pad;
+#pragma unroll
+  for (int j = 0; j < kNT; ++j) {
+    if (rt0 + j >= a.rt16) continue;
+    const int r = (rt0 + j) * 16 + n;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = m * 16 + 4 * kg + i;
+        if (b < a.batch) mine[int64_t(b) * a.rows_pad + r] = yacc[m][j][i];
+      }
+  }
+}
+
+
 // Split-K partials -> y: one thread per output, splits summed in split order.
 __global__ __launch_bounds__(kThreads) void w4a16_reduce_kernel(
     const float *__restrict__ part, int32_t splits, int32_t batch, int32_t rows,
@@ -637,6 +815,26 @@ W4Plan plan_for(const Geometry &g, int bc, int cus) {
   return p;
 }
 
+// Pipelined kernel: the same tiles and splits, chunks of a power of two
+// steps (at most 4; 2 from three slabs up, and for groups below 128 from two
+// slabs down), two of them staged.  Taken when the plain kernel would walk
+// three or more chunks per split.
+W4Plan plan_pipe(const Geometry &g, int bc, int cus) {
+  W4Plan p = plan_for(g, bc, cus);
+  int ns_cap = std::min(kMaxNs / 2, kStageChunks / 2 / p.mt);
+  if (g.group < kStep && p.mt <= 2) ns_cap = std::min(ns_cap, 2);
+  p.ns_max = std::min(p.base + (p.rem ? 1 : 0), ns_cap);
+  while (p.ns_max & (p.ns_max - 1)) p.ns_max &= p.ns_max - 1;   // a power of two
+  p.ns_t = p.ns_max <= 2 ? 2 : 4;
+  p.lds = 2 * size_t(16) * p.mt * (size_t(p.ns_max) * kStep + 8) * 2;
+  return p;
+}
+
+bool use_pipe(const W4Plan &p) {
+  const int steps = p.base + (p.rem ? 1 : 0);
+  return (steps + p.ns_max - 1) / p.ns_max >= 3;
+}
+
 size_t partial_bytes(const Geometry &g, int bc, int cus) {
   if (rows_plan(g, bc, cus).waves) return 0;
   const W4Plan p = plan_for(g, bc, cus);
@@ -674,6 +872,23 @@ gptq_status launch_gemm_sps(const W4Args &a, const W4Plan &p, int sps, hipStream
     case 1: return launch_gemm_ns<MT, 1>(a, p, stream);
     case 2: return launch_gemm_ns<MT, 2>(a, p, stream);
     default: return launch_gemm_ns<MT, 4>(a, p, stream);
+  }
+}
+
+template <int MT, int SPS, int NS>
+gptq_status launch_pipe(const W4Args &a, const W4Plan &p, hipStream_t stream) {
+  auto kern = w4a16_gemm_pipe_kernel<MT, SPS, NS>;
+  GPTQ_TRY(allow_dynamic_lds(reinterpret_cast<const void *>(kern), 96 * 1024));
+  return launch("w4a16_gemm", kern, dim3(p.tiles * p.splits), dim3(kThreads), p.lds, stream, a);
+}
+
+template <int MT>
+gptq_status launch_pipe_sps(const W4Args &a, const W4Plan &p, int sps, hipStream_t stream) {
+  const bool n2 = p.ns_t == 2;
+  switch (sps) {
+    case 1: return n2 ? launch_pipe<MT, 1, 2>(a, p, stream) : launch_pipe<MT, 1, 4>(a, p, stream);
+    case 2: return n2 ? launch_pipe<MT, 2, 2>(a, p, stream) : launch_pipe<MT, 2, 4>(a, p, stream);
+    default: return n2 ? launch_pipe<MT, 4, 2>(a, p, stream) : launch_pipe<MT, 4, 4>(a, p, stream);
   }
 }
 
@@ -794,16 +1009,18 @@ gptq_status gemm_launches(const gptq_w4a16_layer *layer, const uint16_t *x, int6
       GPTQ_TRY(launch_rows_sps(a, rp, sps, s));
       continue;
     }
-    const W4Plan p = plan_for(g, bc, cus);
+    W4Plan p = plan_for(g, bc, cus);
+    const bool pipe = use_pipe(p);
+    if (pipe) p = plan_pipe(g, bc, cus);
     a.splits = p.splits;
     a.base = p.base;
     a.rem = p.rem;
     a.ns_max = p.ns_max;
     switch (p.mt) {
-      case 1: GPTQ_TRY(launch_gemm_sps<1>(a, p, sps, s)); break;
-      case 2: GPTQ_TRY(launch_gemm_sps<2>(a, p, sps, s)); break;
-      case 3: GPTQ_TRY(launch_gemm_sps<3>(a, p, sps, s)); break;
-      default: GPTQ_TRY(launch_gemm_sps<4>(a, p, sps, s)); break;
+      case 1: GPTQ_TRY(pipe ? launch_pipe_sps<1>(a, p, sps, s) : launch_gemm_sps<1>(a, p, sps, s)); break;
+      case 2: GPTQ_TRY(pipe ? launch_pipe_sps<2>(a, p, sps, s) : launch_gemm_sps<2>(a, p, sps, s)); break;
+      case 3: GPTQ_TRY(pipe ? launch_pipe_sps<3>(a, p, sps, s) : launch_gemm_sps<3>(a, p, sps, s)); break;
+      default: GPTQ_TRY(pipe ? launch_pipe_sps<4>(a, p, sps, s) : launch_gemm_sps<4>(a, p, sps, s)); break;
     }
     if (p.splits > 1) {
       const int64_t total = int64_t(bc) * g.rows;
