@@ -624,12 +624,16 @@ __global__ __launch_bounds__(kThreads) void w4a16_reduce_kernel(
   const int b = int(e / rows), r = int(e - int64_t(b) * rows);
   const float *p = part + int64_t(b) * rows_pad + r;
   const int64_t sstride = int64_t(batch) * rows_pad;
-  constexpr int kLoads = 16;   // partials in flight per thread
+  constexpr int kLoads = 8;   // partials in flight per thread, at most
   float sum = 0.f;
   for (int s0 = 0; s0 < splits; s0 += kLoads) {
+    // (s0 + i < splits is the same for every thread: no load past the splits)
     float v[kLoads];
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) v[i] = p[int64_t(min(s0 + i, splits - 1)) * sstride];
+    for (int i = 0; i < kLoads; ++i) {
+      v[i] = 0.f;
+      if (s0 + i < splits) v[i] = p[int64_t(s0 + i) * sstride];
+    }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
       if (s0 + i < splits) sum += v[i];
