@@ -23,7 +23,8 @@ namespace gptq {
 namespace {
 
 constexpr int kNB = 128;          // diagonal block of the factorization
-constexpr int64_t kPanel = 512;   // columns per deferred trailing update
+constexpr int64_t kPanel = 1024;  // columns per deferred trailing update
+constexpr int64_t kSub = 256;      // columns per sub-panel inside a panel
 
 struct Node {
   int b0, bm, b1, height;
@@ -641,35 +642,51 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
   const size_t lds = kDiagLds;
   GPTQ_TRY(allow_dynamic_lds((const void *)potrf_inv_block_kernel, lds));
   const int cus = device_cu_count();
-  // Two levels: the trailing update inside a panel of kPanel columns is
-  // applied after each diagonal block (K = 128), the update of the columns
-  // past the panel once per panel (K = kPanel).
+  // Three levels: inside a sub-panel of kSub columns the trailing update
+  // follows each diagonal block (K = 128); past a sub-panel, the rest of its
+  // panel is updated once (K = kSub); past a panel of kPanel columns, the
+  // rest of the matrix once (K = kPanel).
   for (int64_t c0 = 0; c0 < d; c0 += kPanel) {
     const int64_t c1 = std::min<int64_t>(c0 + kPanel, d);
-    for (int64_t k0 = c0; k0 < c1; k0 += kNB) {
-      const int m = (int)std::min<int64_t>(kNB, d - k0);
-      const int64_t r = d - k0 - m;
-      // The panel below the block is solved in the same launch when its
-      // 64-row slices, plus the block's own workgroup, fit in one round of
-      // the chip (every workgroup factors the block; a second round would
-      // repeat that on the critical path).
-      const int64_t slices = r > 0 ? cdiv(r, 64) : 0;
-      const bool fused = slices > 0 && (d & 3) == 0 && 1 + slices <= cus;
-      GPTQ_TRY(launch("chol_diag_block", potrf_inv_block_kernel,
-                      dim3(unsigned(fused ? 1 + slices : 1)), dim3(kDiagThreads), lds, stream, A,
-                      d, k0, m, flag));
-      if (r <= 0) break;
-      float *A21 = A + (k0 + m) * d + k0;
-      // L21 = A21 * L11^-T   (in place: each workgroup owns whole rows)
-      if (!fused)
-        GPTQ_TRY(gemm_f32(A21, d, A + k0 * d + k0, d, A21, d, (int)r, m, m, 1.f, 0.f, 1, 0, 0, 0,
-                          stream, "chol_trsm"));
-      // the rest of the panel: A[k0+m:, k0+m:c1] -= L21 L21[0:c1-k0-m]^T
-      // (the part of it above the diagonal is written too, and never read)
-      const int64_t nn = c1 - (k0 + m);
-      if (nn > 0)
-        GPTQ_TRY(gemm_f32(A21, d, A21, d, A + (k0 + m) * d + (k0 + m), d, (int)r, (int)nn, m,
-                          -1.f, 1.f, 1, 0, 0, 0, stream, "chol_near"));
+    for (int64_t s0 = c0; s0 < c1; s0 += kSub) {
+      const int64_t s1 = std::min<int64_t>(s0 + kSub, c1);
+      bool last = false;
+      for (int64_t k0 = s0; k0 < s1; k0 += kNB) {
+        const int m = (int)std::min<int64_t>(kNB, d - k0);
+        const int64_t r = d - k0 - m;
+        // The panel below the block is solved in the same launch when its
+        // 64-row slices, plus the block's own workgroup, fit in one round of
+        // the chip (every workgroup factors the block; a second round would
+        // repeat that on the critical path).
+        const int64_t slices = r > 0 ? cdiv(r, 64) : 0;
+        const bool fused = slices > 0 && (d & 3) == 0 && 1 + slices <= cus;
+        GPTQ_TRY(launch("chol_diag_block", potrf_inv_block_kernel,
+                        dim3(unsigned(fused ? 1 + slices : 1)), dim3(kDiagThreads), lds, stream, A,
+                        d, k0, m, flag));
+        if (r <= 0) {
+          last = true;
+          break;
+        }
+        float *A21 = A + (k0 + m) * d + k0;
+        // L21 = A21 * L11^-T   (in place: each workgroup owns whole rows)
+        if (!fused)
+          GPTQ_TRY(gemm_f32(A21, d, A + k0 * d + k0, d, A21, d, (int)r, m, m, 1.f, 0.f, 1, 0, 0, 0,
+                            stream, "chol_trsm"));
+        // the rest of the sub-panel: A[k0+m:, k0+m:s1] -= L21 L21[0:s1-k0-m]^T
+        // (the part of it above the diagonal is written too, and never read)
+        const int64_t nn = s1 - (k0 + m);
+        if (nn > 0)
+          GPTQ_TRY(gemm_f32(A21, d, A21, d, A + (k0 + m) * d + (k0 + m), d, (int)r, (int)nn, m,
+                            -1.f, 1.f, 1, 0, 0, 0, stream, "chol_near"));
+      }
+      if (last) break;
+      // the rest of the panel past the sub-panel: A[s1:, s1:c1] -= Ls Ls[0:c1-s1]^T
+      const int64_t nm = c1 - s1, rm = d - s1;
+      if (nm > 0 && rm > 0) {
+        const float *Ls = A + s1 * d + s0;
+        GPTQ_TRY(gemm_f32(Ls, d, Ls, d, A + s1 * d + s1, d, (int)rm, (int)nm, (int)(s1 - s0),
+                          -1.f, 1.f, 1, 0, 0, 0, stream, "chol_mid"));
+      }
     }
     // the columns past the panel: A22 -= Lp Lp^T (lower triangle), K = c1 - c0
     const int64_t r2 = d - c1;
