@@ -148,6 +148,22 @@ def inverse_cholesky_upper_ul(Hp: np.ndarray) -> np.ndarray:
     return np.triu(U)
 
 
+def unit_upper_factor(Hp: np.ndarray) -> np.ndarray:
+    """T unit upper triangular with Hp = T D T^T, D diagonal and positive.
+
+    The same reversed factor as above without its inverse: Hp = R R^T with R
+    upper (R = J chol(J Hp J) J), then T = R diag(R)^-1 (column k of R divided
+    by R_kk) and D = diag(R)^2.  Since U = R^-1, T = U^-1 diag(U): the
+    compensation of "Komponenty" written with the factor of the Hessian
+    itself rather than of its inverse.  Raises NotSPD like the routes above."""
+    try:
+        Lr = np.linalg.cholesky(Hp[::-1, ::-1])
+    except np.linalg.LinAlgError as exc:
+        raise NotSPD(str(exc)) from exc
+    R = Lr[::-1, ::-1]
+    return np.triu(R / np.diag(R)[None, :])
+
+
 # --------------------------------------------------------------------------
 # Grids.  Decisions in float32 (the kernel's precision), see module header.
 # --------------------------------------------------------------------------

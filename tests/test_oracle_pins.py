@@ -83,6 +83,37 @@ def test_U_is_upper_cholesky_of_inverse(d):
     np.testing.assert_allclose(O.inverse_cholesky_upper_ul(Hp), U, rtol=1e-9, atol=1e-12)
 
 
+@pytest.mark.parametrize("d", [1, 2, 7, 64, 257])
+def test_unit_factor_reconstructs_hessian(d):
+    """T unit upper triangular and Hp = T D T^T with D diagonal, positive:
+    checked by reconstruction, then against the literal route's U through
+    T = U^-1 diag(U) (a linear solve, not the oracle's own formula)."""
+    rng = np.random.default_rng(100 + d)
+    X = rng.standard_normal((d, 3 * d + 5))
+    Hp = O.damped_processing_hessian(O.hessian([X]), O.hessian_diag([X]), np.arange(d), 0.01)
+    T = O.unit_upper_factor(Hp)
+    assert np.all(np.tril(T, -1) == 0)
+    np.testing.assert_array_equal(np.diag(T), np.ones(d))
+    # D from the last row upwards: Tinv Hp Tinv^T must be diagonal
+    Ti = np.linalg.solve(T, np.eye(d))
+    Dm = Ti @ Hp @ Ti.T
+    np.testing.assert_allclose(Dm - np.diag(np.diag(Dm)), 0.0, atol=1e-9 * np.abs(Hp).max())
+    assert np.all(np.diag(Dm) > 0)
+    U = O.inverse_cholesky_upper(Hp)
+    np.testing.assert_allclose(np.linalg.solve(U, np.eye(d)) * np.diag(U)[None, :], T,
+                               rtol=1e-8, atol=1e-10)
+
+
+def test_unit_factor_two_by_two_closed_form():
+    # Hp = [[a, b], [b, c]] = T D T^T with T = [[1, t], [0, 1]]:
+    # c = D_1, b = t D_1, a = D_0 + t^2 D_1  ->  t = b / c
+    a, b, c = 5.0, -1.5, 2.0
+    T = O.unit_upper_factor(np.array([[a, b], [b, c]]))
+    np.testing.assert_allclose(T, [[1.0, b / c], [0.0, 1.0]], rtol=1e-15)
+    with pytest.raises(O.NotSPD):
+        O.unit_upper_factor(np.diag([1.0, -1.0]))
+
+
 def test_U_not_spd_raises():
     H = np.diag([1.0, -1.0, 2.0])
     with pytest.raises(O.NotSPD):
