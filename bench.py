@@ -294,6 +294,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default=I.HEADLINE, choices=sorted(I.CONFIGS))
     ap.add_argument("--chunk-tokens", type=int, default=32768)
+    ap.add_argument("--route", default="auto", choices=["auto", "inverse", "hessian"],
+                    help="factor carrying the compensation (auto: the Hessian's own factor "
+                         "where the layer allows it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--pmc-calibration", action="store_true",
@@ -342,7 +345,7 @@ def main():
         w.copy_(W0)
     layer = GptqLayer(cfg.rows, cfg.cols, bits=cfg.bits, group=cfg.group, block=cfg.block,
                       act_order=cfg.act_order, percdamp=cfg.percdamp, grid=cfg.grid, device=dev,
-                      search=args.search)
+                      search=args.search, route=args.route)
     out = layer.alloc_outputs()
     packed_q = torch.empty((cfg.rows, cfg.cols * cfg.bits // 32), dtype=torch.int32, device=dev)
     packed_z = None
@@ -445,7 +448,7 @@ def main():
         "config": {"workload": cfg.name, "rows": cfg.rows, "cols": cfg.cols,
                    "tokens": cfg.tokens, "chunk_tokens": chunk, "bits": cfg.bits,
                    "group": cfg.group, "block": cfg.block, "act_order": cfg.act_order,
-                   "grid": cfg.grid, "percdamp": cfg.percdamp, "search": args.search},
+                   "grid": cfg.grid, "percdamp": cfg.percdamp, "search": args.search, "route": layer.route},
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
     }
     print(json.dumps(line), flush=True)

@@ -72,6 +72,26 @@ typedef enum {
                            weights); Q4_K for bits = 4                        */
 } gptq_grid;
 
+/* Factor that carries the compensation between gptq_prepare_hinv and
+ * gptq_quantize_layer ("GPTQ", section Komponenty: the not yet quantized
+ * weights are corrected through the Cholesky factor of the inverse Hessian).
+ *
+ * INVERSE: U, the upper Cholesky factor of Hp^-1 (U^T U = Hp^-1), the pages'
+ *   own object; after column j the later columns take w_k -= e_j U_jk with
+ *   e_j = (w_j - w^_j) / U_jj.
+ * HESSIAN: the same compensation without the inverse of the whole factor.
+ *   With Hp = R R^T (R upper, R = U^-1) and T = R diag(R)^-1 (unit upper,
+ *   Hp = T diag(R)^2 T^T), the errors satisfy W - W^ = E U, so E = (W - W^) R
+ *   and a column's compensated weight is w_k = o_k + sum_{j<k} (o_j - w^_j)
+ *   T_jk, o being the weights before compensation.  Updates between blocks
+ *   of 128 columns go through T; inside a block the pages' rule runs on U's
+ *   128 x 128 diagonal block (which the blocked Cholesky forms anyway), from
+ *   the block's compensated weights c = o + z U_BB, z_j = (y_j - o_j) R_jj,
+ *   y the weights carried by T.  Needs cols % 128 == 0, block = 128 and the
+ *   affine grid with group dividing 128 (a group's grid is then chosen inside
+ *   one block). */
+typedef enum { GPTQ_ROUTE_INVERSE = 0, GPTQ_ROUTE_HESSIAN = 1 } gptq_route;
+
 /* Hyper-parameters ("GPTQ", section Hiperparametry: target precision, weights
  * per scale, activation order, value added to the Hessian diagonal). */
 typedef struct {
@@ -95,6 +115,8 @@ typedef struct {
                         each sub-block's (scale, min) among (1 - k/32) x its
                         min-max pair, before the super-block level codes
                         them.                                                 */
+  int32_t route;     /* gptq_route: which triangular factor carries the
+                        compensation (same codes and W^ in exact arithmetic) */
 } gptq_params;
 
 /* Message of the last failing call on this thread ("" if none). */
@@ -153,10 +175,12 @@ gptq_status gptq_hessian_accumulate(float *H, double *hdiag, int64_t d,
  *            its H_ii is taken as 1 and its weights as 0).
  *  perm      out, d int32: perm[p] = original column processed at position p.
  *            act_order: decreasing hdiag, ties by lower index; else identity.
- *  U         out, d x d float, row-major, in processing order: the upper
- *            triangular factor with positive diagonal and U^T U = Hp^-1,
- *            Hp = P (H with dead fix) P^T + percdamp * mean(diag) * I.  The
- *            strict lower triangle is written as 0.
+ *  U         out, d x d float, row-major, in processing order, strict lower
+ *            triangle written as 0.  Hp = P (H with dead fix) P^T + percdamp *
+ *            mean(diag) * I.  route INVERSE: the upper triangular factor with
+ *            positive diagonal and U^T U = Hp^-1.  route HESSIAN (d % 128 ==
+ *            0): U's entries inside the 128 x 128 diagonal blocks, and T's
+ *            (T unit upper with Hp = T D T^T, D diagonal) above them.
  *  ws        scratch, >= gptq_workspace_bytes(., d, p).
  *
  * Synchronizes `stream` once at the end to read the positive-definiteness
@@ -179,7 +203,8 @@ gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d,
  *
  *  W        in/out, rows x cols float, original column order.  On return it
  *           holds the dequantized weights W^ (what the layer uses next).
- *  U, perm, dead  from gptq_prepare_hinv with the same d and params.
+ *  U, perm, dead  from gptq_prepare_hinv with the same d and params (the
+ *           same route).
  *  hdiag    the activation energy from gptq_hessian_accumulate (cols doubles,
  *           original order); read only when params->search is 1, else may be
  *           NULL.

@@ -42,14 +42,19 @@ class gptq_params(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("act_order", ctypes.c_int32),
                 ("percdamp", ctypes.c_float), ("grid", ctypes.c_int32),
-                ("search", ctypes.c_int32)]
+                ("search", ctypes.c_int32), ("route", ctypes.c_int32)]
+
+
+ROUTES = {"inverse": 0, "hessian": 1}
 
 
 def make_params(bits: int, group: int, block: int, act_order: bool, percdamp: float,
-                grid: str | int = "affine", search: bool = False) -> gptq_params:
+                grid: str | int = "affine", search: bool = False,
+                route: str | int = "inverse") -> gptq_params:
     g = grid if isinstance(grid, int) else {"affine": GPTQ_GRID_AFFINE, "q4k": GPTQ_GRID_Q4K}[grid]
+    rt = route if isinstance(route, int) else ROUTES[route]
     return gptq_params(int(bits), int(group), int(block), int(bool(act_order)), float(percdamp), g,
-                       int(bool(search)))
+                       int(bool(search)), rt)
 
 
 class gptq_w4a16_layer(ctypes.Structure):

@@ -161,6 +161,17 @@ static gptq_status check_params(const gptq_params *p, int64_t cols) {
     return fail(GPTQ_ERR_INVALID_ARG, "cols must be a multiple of group");
   if (p->search != 0 && p->search != 1)
     return fail(GPTQ_ERR_INVALID_ARG, "search must be 0 or 1");
+  if (p->route != GPTQ_ROUTE_INVERSE && p->route != GPTQ_ROUTE_HESSIAN)
+    return fail(GPTQ_ERR_INVALID_ARG, "route must be GPTQ_ROUTE_INVERSE or GPTQ_ROUTE_HESSIAN");
+  if (p->route == GPTQ_ROUTE_HESSIAN) {
+    if (p->block != 128)
+      return fail(GPTQ_ERR_INVALID_ARG, "the Hessian-factor route needs block = 128");
+    if (p->grid != GPTQ_GRID_AFFINE || 128 % p->group != 0)
+      return fail(GPTQ_ERR_INVALID_ARG,
+                  "the Hessian-factor route needs the affine grid with group dividing 128");
+    if (cols > 0 && cols % 128 != 0)
+      return fail(GPTQ_ERR_INVALID_ARG, "the Hessian-factor route needs cols % 128 == 0");
+  }
   return GPTQ_OK;
 }
 
@@ -226,6 +237,8 @@ gptq_status gptq_prepare_hinv(const float *H, const double *hdiag, int64_t d,
                               void *ws, size_t ws_bytes, void *stream) {
   if (d < 1 || d > kMaxDim) return fail(GPTQ_ERR_INVALID_ARG, "d must be in [1, 2^20]");
   GPTQ_TRY(check_params(p, 0));
+  if (p->route == GPTQ_ROUTE_HESSIAN && d % 128 != 0)
+    return fail(GPTQ_ERR_INVALID_ARG, "the Hessian-factor route needs d % 128 == 0");
   if (!H || !hdiag || !U || !perm || !dead)
     return fail(GPTQ_ERR_INVALID_ARG, "H, hdiag, U, perm and dead must not be NULL");
   if (!aligned(H, 16) || !aligned(U, 16))

@@ -555,6 +555,31 @@ __global__ void __launch_bounds__(kDiagThreads)
   }
 }
 
+// Hessian-factor route.  After the blocked Cholesky A holds L below its
+// 128 x 128 diagonal blocks and L_kk^-1 in them.  With R = J L J (Hp = R R^T)
+// and U = R^-1:
+//   F[i][j] = U_ij = Linv[a][b]             a, b in one diagonal block,
+//   F[i][j] = T_ij = R_ij / R_jj = L[a][b] / L[b][b] = L[a][b] Linv[b][b]
+//                                          otherwise,
+// a = d-1-i, b = d-1-j, j >= i; 0 below the diagonal.  Thread t owns one
+// column j for every row it visits; its divisor Linv[b][b] is read once.
+__global__ void __launch_bounds__(256)
+    rotate_factor_kernel(const float *__restrict__ A, int64_t d, float *__restrict__ F) {
+  const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= d) return;
+  const int64_t b = d - 1 - j;
+  const float rdiag = A[b * d + b];
+  for (int64_t i = blockIdx.y; i < d; i += gridDim.y) {
+    const int64_t a = d - 1 - i;
+    float v = 0.f;
+    if (j >= i) {
+      const float l = A[a * d + b];
+      v = (a / kNB == b / kNB) ? l : l * rdiag;
+    }
+    F[i * d + j] = v;
+  }
+}
+
 // U[i][j] = Linv[d-1-i][d-1-j] for j >= i, 0 below the diagonal.
 __global__ void __launch_bounds__(256)
     rotate_upper_kernel(const float *__restrict__ Linv, int64_t d, float *__restrict__ U) {
@@ -697,6 +722,14 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
     }
   }
 
+  if (p.route == GPTQ_ROUTE_HESSIAN) {
+    // no inverse past the diagonal blocks: U's blocks there, T above them
+    GPTQ_TRY(launch("prep_rotate", rotate_factor_kernel,
+                    dim3((unsigned)cdiv(d, 256), (unsigned)std::min<int64_t>(d, 2048)), dim3(256),
+                    0, stream, (const float *)A, d, U));
+    hmax = 0;
+  }
+
   // ---- recursive triangular inverse, bottom-up by tree height:
   //   T = L21 X11 ; X21 = -X22 T   (X11, X22 already inverted)
   for (int h = 1; h <= hmax; ++h) {
@@ -748,7 +781,9 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
     }
   }
 
-  if ((d & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0 &&
+  if (p.route == GPTQ_ROUTE_HESSIAN) {
+    // written above
+  } else if ((d & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0 &&
       (reinterpret_cast<uintptr_t>(A) & 15) == 0)
     GPTQ_TRY(launch("prep_rotate", rotate_upper_vec_kernel,
                     dim3((unsigned)std::min<int64_t>(cdiv(d / 4, 256), 64),

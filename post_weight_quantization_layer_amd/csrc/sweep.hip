@@ -42,6 +42,11 @@ struct SweepArgs {
   float *Err;      // the super-block's first column of the error buffer, ld = ldE
   int ldE;
   const float *U;  // ld = cols
+  // Hessian-factor route (null on the inverse-factor route): the weights
+  // before any compensation, processing order, ld = cols.  U then holds the
+  // unit factor T off its diagonal B x B blocks and the inverse factor's
+  // blocks on them (B = 128).
+  const float *Wo;
   int64_t rows, cols;
   int s1, B, nblk; // nblk blocks of B columns from column s1 (the last may be shorter)
   int gblk;        // blocks per group when a group spans several blocks of a launch, else 1
@@ -174,7 +179,7 @@ __device__ __forceinline__ void static_for(F &&f) {
 // kG8: the group size is a multiple of 8, so groups start only at the first
 // column of an 8-column step (the check runs once per 8 columns).
 // One block [i1, i1 + B) of the sweep for all of this workgroup's rows.
-template <int kQ4K, bool kG8>
+template <int kQ4K, bool kG8, bool kH>
 __device__ __forceinline__ void sweep_block(const SweepArgs &a, const int i1, const int B,
                                             float *const Err) {
   // LDS: U's block (rows 0 .. Bp+1 of kMaxB floats, Bp = B rounded up to 8,
@@ -204,7 +209,13 @@ __device__ __forceinline__ void sweep_block(const SweepArgs &a, const int i1, co
 
   // The first row group's weights are requested before the U block, so the
   // two latencies overlap.
-  float w[kCPL];
+  // w: current weights of this lane's 8 block columns; o: the same columns
+  // before any compensation (Hessian-factor route only)
+  float w[kCPL], o[kCPL] = {};
+  // Hessian-factor route (a.Wo set).  Tested at run time as well: as a
+  // branch the conversion below stays a region of its own, which the
+  // scheduler does not interleave with the sweep (fused, the kernel spills)
+  const bool hroute = kH && a.Wo != nullptr;
   auto load_w = [&](int64_t r0) {
     const int64_t rowc = min(r0 + grp, a.rows - 1);
     const float *wrow = a.W + rowc * ld + i1;
@@ -215,6 +226,16 @@ __device__ __forceinline__ void sweep_block(const SweepArgs &a, const int i1, co
       for (int x = 0; x < 4; ++x) {
         w[x] = t0[x];
         w[4 + x] = t1[x];
+      }
+      if (hroute) {
+        const float *orow = a.Wo + rowc * ld + i1;
+        const f32x4_t v0 = *reinterpret_cast<const f32x4_t *>(orow + c0);
+        const f32x4_t v1 = *reinterpret_cast<const f32x4_t *>(orow + c0 + 4);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          o[x] = v0[x];
+          o[4 + x] = v1[x];
+        }
       }
     } else {
 #pragma unroll
@@ -278,6 +299,53 @@ __device__ __forceinline__ void sweep_block(const SweepArgs &a, const int i1, co
     const bool rv = row < a.rows;  // whole row group is valid or not
     const int64_t rowc = rv ? row : a.rows - 1;
     float *wrow = a.W + rowc * ld + i1;
+
+    if (hroute) {
+      // Hessian-factor route.  The loaded weights are y_k = o_k + sum_{i<k}
+      // (o_i - w^_i) T_ik over the columns before the block: exact for the
+      // block's first column, but the grid of a group is chosen from the
+      // compensated weights of all its columns with the earlier columns
+      // fixed, c = o + z U_BB with z_j = (y_j - o_j) R_jj (R_jj = 1 / U_jj,
+      // U_BB the inverse factor's diagonal block).  The block is then swept
+      // from c by the inverse-factor rule inside the block.
+      const f32x4_t d0 = *reinterpret_cast<const f32x4_t *>(Uinv + c0);
+      const f32x4_t d1 = *reinterpret_cast<const f32x4_t *>(Uinv + c0 + 4);
+      float zl[kCPL], cv[kCPL];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        zl[y] = (w[y] - o[y]) * d0[y];
+        zl[4 + y] = (w[4 + y] - o[4 + y]) * d1[y];
+      }
+#pragma unroll
+      for (int y = 0; y < kCPL; ++y) cv[y] = o[y];
+      // U_BB's rows are the same for every row pass: an opaque column offset
+      // keeps their reads in the pass (hoisted out of it they would need
+      // every row at once, and spill)
+      int cu = c0;
+      asm volatile("" : "+v"(cu));
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, kMaxB / kCPL>([&](auto ow) {
+        constexpr int kOw = decltype(ow)::value;
+        static_for<0, kCPL>([&](auto xs) {
+          constexpr int x = decltype(xs)::value;
+          constexpr int j = kOw * kCPL + x;
+          const f32x4_t u0 = *reinterpret_cast<const f32x4_t *>(Ub + j * kMaxB + cu);
+          const f32x4_t u1 = *reinterpret_cast<const f32x4_t *>(Ub + j * kMaxB + cu + 4);
+          const float zj = row_bcast<kOw>(zl[x]);
+#pragma unroll
+          for (int yy = 0; yy < 4; ++yy) {
+            cv[yy] = fmaf(zj, u0[yy], cv[yy]);
+            cv[4 + yy] = fmaf(zj, u1[yy], cv[4 + yy]);
+          }
+        });
+        // one owner's 8 rows of U_BB in flight at a time (hoisting every
+        // read of the unrolled loop would spill)
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int y = 0; y < kCPL; ++y) w[y] = cv[y];
+    }
 
     // grid state of the current group (per row group, identical in its lanes)
     float s = 1.f, rs = 1.f, z = 0.f;       // affine
@@ -486,6 +554,12 @@ __device__ __forceinline__ void sweep_block(const SweepArgs &a, const int i1, co
       if (!(rv && sl == (j8 >> 3))) return;
       uint8_t *qrow = a.q + row * ld + i1;
       float *erow = Err + row * a.ldE;
+      // Hessian-factor route: the later columns take the error against the
+      // uncompensated weight, w^_j - o_j, through T
+      if (hroute) {
+#pragma unroll
+        for (int x = 0; x < kCPL; ++x) et[x] = wt[x] - o[x];
+      }
       if (full && evec) {
         *reinterpret_cast<f32x4_t *>(wrow + c0) = f32x4_t{wt[0], wt[1], wt[2], wt[3]};
         *reinterpret_cast<f32x4_t *>(wrow + c0 + 4) = f32x4_t{wt[4], wt[5], wt[6], wt[7]};
@@ -757,7 +831,7 @@ __device__ __forceinline__ void near_update(const SweepArgs &a, const int i1, co
 // updates of the group's own earlier blocks at their turn.  A workgroup
 // keeps the same rows throughout and reads only the errors it wrote, so
 // the blocks need no synchronization beyond the workgroup's own barriers.
-template <int kQ4K, bool kG8>
+template <int kQ4K, bool kG8, bool kH>
 __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
   for (int blk = 0; blk < a.nblk; ++blk) {
     const int i1 = a.s1 + blk * a.B;
@@ -775,7 +849,7 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepArgs a) {
       }
       __syncthreads();   // the updated weights are visible to every wave
     }
-    sweep_block<kQ4K, kG8>(a, i1, B, a.Err + blk * a.B);
+    sweep_block<kQ4K, kG8, kH>(a, i1, B, a.Err + blk * a.B);
   }
 }
 
@@ -920,6 +994,8 @@ size_t quantize_ws_bytes(int64_t rows, int64_t cols, const gptq_params &p) {
     n += align256(size_t(rows) * size_t(cols));                  // qp
   }
   if (p.search) n += align256(size_t(cols) * sizeof(double));    // importances, processing order
+  if (p.route == GPTQ_ROUTE_HESSIAN)
+    n += align256(size_t(rows) * size_t(cols) * sizeof(float));  // uncompensated weights
   return n;
 }
 
@@ -972,6 +1048,19 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
                     W, rows, cols, dead));
   }
 
+  // Hessian-factor route: the weights before any compensation, kept beside
+  // the working copy (processing order, dead columns zeroed)
+  const float *Wo = nullptr;
+  if (p.route == GPTQ_ROUTE_HESSIAN) {
+    float *o = reinterpret_cast<float *>(base);
+    base += align256(size_t(rows) * size_t(cols) * sizeof(float));
+    const hipError_t e = hipMemcpyAsync(o, Wp, size_t(rows) * size_t(cols) * sizeof(float),
+                                        hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess)
+      return fail(GPTQ_ERR_DEVICE, std::string("quantize_layer: ") + hipGetErrorString(e));
+    Wo = o;
+  }
+
   const double *hp = nullptr;
   if (p.search) {
     double *h = reinterpret_cast<double *>(base);
@@ -987,10 +1076,15 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   const size_t lds = ((Bp + 2) * kMaxB + Bp + 2 + 1) * sizeof(float) +
                      (p.search ? size_t(B) * sizeof(double) : 0);
   const int g8 = (q4k ? 256 : p.group) % 8 == 0;
-  const int variant = q4k * 2 + g8;
+  const int hr = p.route == GPTQ_ROUTE_HESSIAN;   // affine only (checked by the caller)
+  const int variant = hr ? 4 + g8 : q4k * 2 + g8;
   // (Q4_K groups are 256 columns, always a multiple of 8: variant 3)
-  const void *kfn[4] = {(const void *)sweep_kernel<0, false>, (const void *)sweep_kernel<0, true>,
-                        (const void *)sweep_kernel<1, true>, (const void *)sweep_kernel<1, true>};
+  const void *kfn[6] = {(const void *)sweep_kernel<0, false, false>,
+                        (const void *)sweep_kernel<0, true, false>,
+                        (const void *)sweep_kernel<1, true, false>,
+                        (const void *)sweep_kernel<1, true, false>,
+                        (const void *)sweep_kernel<0, false, true>,
+                        (const void *)sweep_kernel<0, true, true>};
   // A launch with no more workgroups than compute units gets one per CU (its
   // LDS request is raised past half the CU's LDS), so that each wavefront
   // has a SIMD to itself: the sweep is a chain of dependent steps per row,
@@ -1005,6 +1099,7 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   a.W = Wp;
   a.q = qp;
   a.U = U;
+  a.Wo = Wo;
   a.rows = rows;
   a.cols = cols;
   a.bits = p.bits;
@@ -1057,9 +1152,11 @@ gptq_status quantize_layer_impl(float *W, int64_t rows, int64_t cols, const floa
   const dim3 grid(nwg), blk(kSweepThreads);
   auto sweep_launch = [&]() -> gptq_status {
     switch (variant) {
-      case 0: return launch(nm, sweep_kernel<0, false>, grid, blk, lds_launch, stream, a);
-      case 1: return launch(nm, sweep_kernel<0, true>, grid, blk, lds_launch, stream, a);
-      default: return launch(nm, sweep_kernel<1, true>, grid, blk, lds_launch, stream, a);
+      case 0: return launch(nm, sweep_kernel<0, false, false>, grid, blk, lds_launch, stream, a);
+      case 1: return launch(nm, sweep_kernel<0, true, false>, grid, blk, lds_launch, stream, a);
+      case 4: return launch(nm, sweep_kernel<0, false, true>, grid, blk, lds_launch, stream, a);
+      case 5: return launch(nm, sweep_kernel<0, true, true>, grid, blk, lds_launch, stream, a);
+      default: return launch(nm, sweep_kernel<1, true, false>, grid, blk, lds_launch, stream, a);
     }
   };
   for (int64_t g1 = 0; g1 < cols; g1 += FG) {

@@ -29,17 +29,33 @@ class QuantizedLayer:
     sub_min: torch.Tensor | None = None
 
 
+def fast_route(cols: int, *, group: int, block: int, grid: str = "affine") -> str:
+    """The Hessian-factor route where the library accepts it (affine grid,
+    block 128, group dividing 128, cols a multiple of 128), else the
+    inverse-factor route.  Both reach the same codes in exact arithmetic."""
+    ok = grid == "affine" and block == 128 and 128 % group == 0 and cols % 128 == 0
+    return "hessian" if ok else "inverse"
+
+
 class GptqLayer:
-    """Buffers and call order for quantizing one layer on the current device."""
+    """Buffers and call order for quantizing one layer on the current device.
+
+    ``route``: "inverse" (U, the Cholesky factor of the inverse Hessian),
+    "hessian" (the Hessian's own unit factor between 128-column blocks) or
+    "auto" (fast_route)."""
 
     def __init__(self, rows: int, cols: int, *, bits: int, group: int, block: int,
                  act_order: bool, percdamp: float = 0.01, grid: str = "affine",
-                 device: str = "cuda", search: bool = False):
+                 device: str = "cuda", search: bool = False, route: str = "inverse"):
         self.rows, self.cols = rows, cols
         self.grid = grid
         self.bits = bits
         self.group = 256 if grid == "q4k" else group
-        self.params = B.make_params(bits, self.group, block, act_order, percdamp, grid, search)
+        if route == "auto":
+            route = fast_route(cols, group=self.group, block=block, grid=grid)
+        self.route = route
+        self.params = B.make_params(bits, self.group, block, act_order, percdamp, grid, search,
+                                    route)
         dev = torch.device(device)
         self.device = dev
         self.H = torch.zeros((cols, cols), dtype=torch.float32, device=dev)

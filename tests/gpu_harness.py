@@ -49,15 +49,27 @@ class GpuOut:
     mc: np.ndarray | None = None
 
 
+def expected_factor(U: np.ndarray, H: np.ndarray, diag: np.ndarray, perm: np.ndarray,
+                    percdamp: float, route: str) -> np.ndarray:
+    """What gptq_prepare_hinv writes for a route, from the oracle: U itself
+    (inverse route), or U inside the 128 x 128 diagonal blocks and the unit
+    factor T of the damped Hessian above them (Hessian route)."""
+    if route == "inverse":
+        return U
+    T = O.unit_upper_factor(O.damped_processing_hessian(H, diag, perm, percdamp))
+    b = np.arange(U.shape[0]) // 128
+    return np.where(b[:, None] == b[None, :], U, T)
+
+
 def gpu_layer(cfg: I.LayerConfig, W: np.ndarray, chunks, dev="cuda", keep_H=True,
-              search=False) -> GpuOut:
+              search=False, route="inverse") -> GpuOut:
     """chunks: iterable of storage-dtype X chunks (d x n_c)."""
     import torch
     from post_weight_quantization_layer_amd import binding as B
     from post_weight_quantization_layer_amd.layer import GptqLayer
     L = GptqLayer(W.shape[0], cfg.cols, bits=cfg.bits, group=cfg.group, block=cfg.block,
                   act_order=cfg.act_order, percdamp=cfg.percdamp, grid=cfg.grid, device=dev,
-                  search=search)
+                  search=search, route=route)
     for xs in chunks:
         t, n, ld = to_device_x(xs, dev)
         B.gptq_hessian_accumulate(L.H, L.hdiag, t, n_tok=n, ld_x=ld, ws=L.ws)

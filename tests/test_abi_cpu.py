@@ -56,12 +56,16 @@ FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
     (dict(grid=7), "grid"),
     (dict(group=96, block=32), "multiple of group"),
     (dict(search=2), "search"),
+    (dict(route=2), "route"),
+    (dict(route=1, block=64), "block = 128"),
+    (dict(route=1, grid=1, group=256), "affine grid"),
+    (dict(route=1, group=256, block=128), "affine grid"),
 ])
 def test_quantize_rejects_bad_params(kw, msg):
     base = dict(bits=4, group=128, block=128, act_order=0, percdamp=0.01, grid=0)
     base.update(kw)
     p = B.gptq_params(base["bits"], base["group"], base["block"], base["act_order"],
-                      base["percdamp"], base["grid"], base.get("search", 0))
+                      base["percdamp"], base["grid"], base.get("search", 0), base.get("route", 0))
     L = B.lib()
     st = L.gptq_quantize_layer(FAKE, 64, 1024, FAKE, FAKE, FAKE, FAKE, ctypes.byref(p), FAKE,
                                FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
@@ -198,3 +202,18 @@ def test_weighted_search_needs_hdiag():
     rows = 1 << 20      # the sweep's share of the workspace is the larger one
     n0 = B.gptq_workspace_bytes(rows, 1024, B.make_params(4, 128, 128, False, 0.01))
     assert B.gptq_workspace_bytes(rows, 1024, p) >= n0 + 1024 * 8
+
+
+def test_hessian_route_needs_cols_multiple_of_128():
+    L = B.lib()
+    p = B.make_params(4, 64, 128, False, 0.01, route="hessian")
+    st = L.gptq_quantize_layer(FAKE, 64, 960, FAKE, FAKE, FAKE, FAKE, ctypes.byref(p), FAKE,
+                               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == B.GPTQ_ERR_INVALID_ARG and "128" in B.gptq_last_error()
+    st = L.gptq_prepare_hinv(FAKE, FAKE, 960, ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                             None)
+    assert st == B.GPTQ_ERR_INVALID_ARG and "128" in B.gptq_last_error()
+    # the route keeps the uncompensated weights beside the working copy
+    n_inv = B.gptq_workspace_bytes(4096, 1024, B.make_params(4, 64, 128, False, 0.01))
+    n_h = B.gptq_workspace_bytes(4096, 1024, p)
+    assert n_h - n_inv == 4096 * 1024 * 4
