@@ -561,22 +561,35 @@ __global__ void __launch_bounds__(kDiagThreads)
 //   F[i][j] = U_ij = Linv[a][b]             a, b in one diagonal block,
 //   F[i][j] = T_ij = R_ij / R_jj = L[a][b] / L[b][b] = L[a][b] Linv[b][b]
 //                                          otherwise,
-// a = d-1-i, b = d-1-j, j >= i; 0 below the diagonal.  Thread t owns one
-// column j for every row it visits; its divisor Linv[b][b] is read once.
+// a = d-1-i, b = d-1-j, j >= i; 0 below the diagonal.  Thread t owns the
+// four columns 4t .. 4t+3 (one reversed 16-byte segment of a row of A) for
+// every row it visits; their divisors Linv[b][b] are read once.  d % 4 == 0
+// and 16-byte aligned A and F.
 __global__ void __launch_bounds__(256)
     rotate_factor_kernel(const float *__restrict__ A, int64_t d, float *__restrict__ F) {
-  const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (j >= d) return;
-  const int64_t b = d - 1 - j;
-  const float rdiag = A[b * d + b];
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= d / 4) return;
+  const int64_t j = 4 * t;
+  f32x4_t rdiag;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t b = d - 1 - (j + e);
+    rdiag[e] = A[b * d + b];
+  }
+  const int64_t bblk = (d - 1 - j) / kNB;   // the four columns share one diagonal block
   for (int64_t i = blockIdx.y; i < d; i += gridDim.y) {
-    const int64_t a = d - 1 - i;
-    float v = 0.f;
-    if (j >= i) {
-      const float l = A[a * d + b];
-      v = (a / kNB == b / kNB) ? l : l * rdiag;
+    f32x4_t out = {0.f, 0.f, 0.f, 0.f};
+    if (j + 3 >= i) {
+      const int64_t a = d - 1 - i;
+      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(A + a * d + (d - 4 - j));
+      const bool same = a / kNB == bblk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float l = v[3 - e];
+        out[e] = j + e >= i ? (same ? l : l * rdiag[e]) : 0.f;
+      }
     }
-    F[i * d + j] = v;
+    *reinterpret_cast<f32x4_t *>(F + i * d + j) = out;
   }
 }
 
@@ -725,8 +738,8 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
   if (p.route == GPTQ_ROUTE_HESSIAN) {
     // no inverse past the diagonal blocks: U's blocks there, T above them
     GPTQ_TRY(launch("prep_rotate", rotate_factor_kernel,
-                    dim3((unsigned)cdiv(d, 256), (unsigned)std::min<int64_t>(d, 2048)), dim3(256),
-                    0, stream, (const float *)A, d, U));
+                    dim3((unsigned)cdiv(d / 4, 256), (unsigned)std::min<int64_t>(d, 8192)),
+                    dim3(256), 0, stream, (const float *)A, d, U));
     hmax = 0;
   }
 

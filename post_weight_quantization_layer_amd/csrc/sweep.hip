@@ -318,19 +318,24 @@ __device__ __forceinline__ void sweep_block(const SweepArgs &a, const int i1, co
       }
 #pragma unroll
       for (int y = 0; y < kCPL; ++y) cv[y] = o[y];
-      // U_BB's rows are the same for every row pass: an opaque column offset
-      // keeps their reads in the pass (hoisted out of it they would need
-      // every row at once, and spill)
-      int cu = c0;
-      asm volatile("" : "+v"(cu));
+      // rows j of U_BB read two steps ahead (rows past B are zero in LDS),
+      // as in the column steps below
+      f32x4_t qa0 = *reinterpret_cast<const f32x4_t *>(Ub + c0);
+      f32x4_t qa1 = *reinterpret_cast<const f32x4_t *>(Ub + c0 + 4);
+      f32x4_t qb0 = *reinterpret_cast<const f32x4_t *>(Ub + kMaxB + c0);
+      f32x4_t qb1 = *reinterpret_cast<const f32x4_t *>(Ub + kMaxB + c0 + 4);
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, kMaxB / kCPL>([&](auto ow) {
         constexpr int kOw = decltype(ow)::value;
         static_for<0, kCPL>([&](auto xs) {
           constexpr int x = decltype(xs)::value;
           constexpr int j = kOw * kCPL + x;
-          const f32x4_t u0 = *reinterpret_cast<const f32x4_t *>(Ub + j * kMaxB + cu);
-          const f32x4_t u1 = *reinterpret_cast<const f32x4_t *>(Ub + j * kMaxB + cu + 4);
+          const f32x4_t u0 = qa0, u1 = qa1;
+          qa0 = qb0;
+          qa1 = qb1;
+          qb0 = *reinterpret_cast<const f32x4_t *>(Ub + (j + 2) * kMaxB + c0);
+          qb1 = *reinterpret_cast<const f32x4_t *>(Ub + (j + 2) * kMaxB + c0 + 4);
+          __builtin_amdgcn_sched_barrier(0);
           const float zj = row_bcast<kOw>(zl[x]);
 #pragma unroll
           for (int yy = 0; yy < 4; ++yy) {
@@ -338,9 +343,6 @@ __device__ __forceinline__ void sweep_block(const SweepArgs &a, const int i1, co
             cv[4 + yy] = fmaf(zj, u1[yy], cv[4 + yy]);
           }
         });
-        // one owner's 8 rows of U_BB in flight at a time (hoisting every
-        // read of the unrolled loop would spill)
-        __builtin_amdgcn_sched_barrier(0);
       });
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
