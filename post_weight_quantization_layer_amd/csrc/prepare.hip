@@ -563,7 +563,8 @@ __global__ void __launch_bounds__(kDiagThreads)
 //                                          otherwise,
 // a = d-1-i, b = d-1-j, j >= i; 0 below the diagonal.  Thread t owns the
 // four columns 4t .. 4t+3 (one reversed 16-byte segment of a row of A) for
-// every row it visits; their divisors Linv[b][b] are read once.  d % 4 == 0
+// every row it visits (a short grid in y, so that each thread visits many
+// rows); their divisors Linv[b][b] are read once.  d % 4 == 0
 // and 16-byte aligned A and F.
 __global__ void __launch_bounds__(256)
     rotate_factor_kernel(const float *__restrict__ A, int64_t d, float *__restrict__ F) {
@@ -738,7 +739,7 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
   if (p.route == GPTQ_ROUTE_HESSIAN) {
     // no inverse past the diagonal blocks: U's blocks there, T above them
     GPTQ_TRY(launch("prep_rotate", rotate_factor_kernel,
-                    dim3((unsigned)cdiv(d / 4, 256), (unsigned)std::min<int64_t>(d, 8192)),
+                    dim3((unsigned)cdiv(d / 4, 256), (unsigned)std::min<int64_t>(d, 256)),
                     dim3(256), 0, stream, (const float *)A, d, U));
     hmax = 0;
   }
