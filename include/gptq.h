@@ -80,16 +80,15 @@ typedef enum {
  *   own object; after column j the later columns take w_k -= e_j U_jk with
  *   e_j = (w_j - w^_j) / U_jj.
  * HESSIAN: the same compensation without the inverse of the whole factor.
- *   With Hp = R R^T (R upper, R = U^-1) and T = R diag(R)^-1 (unit upper,
- *   Hp = T diag(R)^2 T^T), the errors satisfy W - W^ = E U, so E = (W - W^) R
- *   and a column's compensated weight is w_k = o_k + sum_{j<k} (o_j - w^_j)
- *   T_jk, o being the weights before compensation.  Updates between blocks
- *   of 128 columns go through T; inside a block the pages' rule runs on U's
- *   128 x 128 diagonal block (which the blocked Cholesky forms anyway), from
- *   the block's compensated weights c = o + z U_BB, z_j = (y_j - o_j) R_jj,
- *   y the weights carried by T.  Needs cols % 128 == 0, block = 128 and the
- *   affine grid with group dividing 128 (a group's grid is then chosen inside
- *   one block). */
+ *   With Hp = R R^T (R upper, R = U^-1) the errors satisfy W - W^ = E U, so
+ *   E = (W - W^) R, and the compensated weights of a block B of 128 columns
+ *   at its turn are c_B = o_B + (o - w^)_{<B} R_{<B,B} U_BB, o being the
+ *   weights before compensation and U_BB U's diagonal block (the inverse of
+ *   R's, which the blocked Cholesky forms anyway).  So the updates between
+ *   blocks go through M = R_{<B,B} U_BB with the error w^_j - o_j, and the
+ *   pages' rule runs inside each block on U_BB.  Needs cols % 128 == 0,
+ *   block = 128 and the affine grid with group dividing 128 (a group's grid
+ *   is then chosen inside one block). */
 typedef enum { GPTQ_ROUTE_INVERSE = 0, GPTQ_ROUTE_HESSIAN = 1 } gptq_route;
 
 /* Hyper-parameters ("GPTQ", section Hiperparametry: target precision, weights
@@ -179,8 +178,9 @@ gptq_status gptq_hessian_accumulate(float *H, double *hdiag, int64_t d,
  *            triangle written as 0.  Hp = P (H with dead fix) P^T + percdamp *
  *            mean(diag) * I.  route INVERSE: the upper triangular factor with
  *            positive diagonal and U^T U = Hp^-1.  route HESSIAN (d % 128 ==
- *            0): U's entries inside the 128 x 128 diagonal blocks, and T's
- *            (T unit upper with Hp = T D T^T, D diagonal) above them.
+ *            0): U's entries inside the 128 x 128 diagonal blocks, and above
+ *            each diagonal block B the product R_{<B,B} U_BB, where Hp =
+ *            R R^T with R upper triangular (R = U^-1).
  *  ws        scratch, >= gptq_workspace_bytes(., d, p).
  *
  * Synchronizes `stream` once at the end to read the positive-definiteness

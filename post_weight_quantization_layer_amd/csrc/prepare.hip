@@ -555,40 +555,26 @@ __global__ void __launch_bounds__(kDiagThreads)
   }
 }
 
-// Hessian-factor route.  After the blocked Cholesky A holds L below its
-// 128 x 128 diagonal blocks and L_kk^-1 in them.  With R = J L J (Hp = R R^T)
-// and U = R^-1:
-//   F[i][j] = U_ij = Linv[a][b]             a, b in one diagonal block,
-//   F[i][j] = T_ij = R_ij / R_jj = L[a][b] / L[b][b] = L[a][b] Linv[b][b]
-//                                          otherwise,
-// a = d-1-i, b = d-1-j, j >= i; 0 below the diagonal.  Thread t owns the
-// four columns 4t .. 4t+3 (one reversed 16-byte segment of a row of A) for
-// every row it visits (a short grid in y, so that each thread visits many
-// rows); their divisors Linv[b][b] are read once.  d % 4 == 0
+// Hessian-factor route, first step.  After the blocked Cholesky A holds L
+// below its 128 x 128 diagonal blocks and L_kk^-1 in them.  With R = J L J
+// (Hp = R R^T) and U = R^-1, processing order, a = d-1-i, b = d-1-j, j >= i:
+//   F[i][j] = U_ij = Linv[a][b]   a, b in one diagonal block,
+//   F[i][j] = R_ij = L[a][b]      otherwise;
+// 0 below the diagonal.  (The second step multiplies each block column of R
+// above the diagonal block by that block, U_BB.)  Thread t owns the four
+// columns 4t .. 4t+3, one reversed 16-byte segment of a row of A; d % 4 == 0
 // and 16-byte aligned A and F.
 __global__ void __launch_bounds__(256)
     rotate_factor_kernel(const float *__restrict__ A, int64_t d, float *__restrict__ F) {
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (t >= d / 4) return;
   const int64_t j = 4 * t;
-  f32x4_t rdiag;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int64_t b = d - 1 - (j + e);
-    rdiag[e] = A[b * d + b];
-  }
-  const int64_t bblk = (d - 1 - j) / kNB;   // the four columns share one diagonal block
   for (int64_t i = blockIdx.y; i < d; i += gridDim.y) {
     f32x4_t out = {0.f, 0.f, 0.f, 0.f};
     if (j + 3 >= i) {
-      const int64_t a = d - 1 - i;
-      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(A + a * d + (d - 4 - j));
-      const bool same = a / kNB == bblk;
+      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(A + (d - 1 - i) * d + (d - 4 - j));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float l = v[3 - e];
-        out[e] = j + e >= i ? (same ? l : l * rdiag[e]) : 0.f;
-      }
+      for (int e = 0; e < 4; ++e) out[e] = j + e >= i ? v[3 - e] : 0.f;
     }
     *reinterpret_cast<f32x4_t *>(F + i * d + j) = out;
   }
@@ -737,10 +723,33 @@ gptq_status prepare_hinv_impl(const float *H, const double *hdiag, int64_t d,
   }
 
   if (p.route == GPTQ_ROUTE_HESSIAN) {
-    // no inverse past the diagonal blocks: U's blocks there, T above them
+    // no inverse past the diagonal blocks: U's blocks there, R above them,
+    // then each block column of R times its diagonal block (in place; the
+    // problems touch disjoint columns): F[0:b0, B] = R[0:b0, B] U_BB
     GPTQ_TRY(launch("prep_rotate", rotate_factor_kernel,
-                    dim3((unsigned)cdiv(d / 4, 256), (unsigned)std::min<int64_t>(d, 256)),
+                    dim3((unsigned)(d / 4 + 255) / 256, (unsigned)std::min<int64_t>(d, 1024)),
                     dim3(256), 0, stream, (const float *)A, d, U));
+    GemmGroup g{};
+    g.transB = 0;
+    for (int64_t b0 = kNB; b0 < d; b0 += kNB) {
+      GemmProblem &q = g.p[g.count++];
+      q.A = U + b0;                  // R[0:b0, B]
+      q.lda = d;
+      q.B = U + b0 * d + b0;         // U_BB
+      q.ldb = d;
+      q.C = U + b0;                  // over R
+      q.ldc = d;
+      q.M = (int)b0;
+      q.N = kNB;
+      q.K = kNB;
+      q.alpha = 1.f;
+      q.beta = 0.f;
+      if (g.count == kMaxGemmGroup || b0 + kNB >= d) {
+        GPTQ_TRY(gemm_f32_grouped(g, stream, "prep_factor_blocks"));
+        g = GemmGroup{};
+        g.transB = 0;
+      }
+    }
     hmax = 0;
   }
 

@@ -44,8 +44,8 @@ struct SweepArgs {
   const float *U;  // ld = cols
   // Hessian-factor route (null on the inverse-factor route): the weights
   // before any compensation, processing order, ld = cols.  U then holds the
-  // unit factor T off its diagonal B x B blocks and the inverse factor's
-  // blocks on them (B = 128).
+  // inverse factor's diagonal blocks U_BB (B = 128), and above each of them
+  // R_{<B,B} U_BB, R the Hessian's reversed Cholesky factor (Hp = R R^T).
   const float *Wo;
   int64_t rows, cols;
   int s1, B, nblk; // nblk blocks of B columns from column s1 (the last may be shorter)
@@ -212,9 +212,9 @@ __device__ __forceinline__ void sweep_block(const SweepArgs &a, const int i1, co
   // w: current weights of this lane's 8 block columns; o: the same columns
   // before any compensation (Hessian-factor route only)
   float w[kCPL], o[kCPL] = {};
-  // Hessian-factor route (a.Wo set).  Tested at run time as well: as a
-  // branch the conversion below stays a region of its own, which the
-  // scheduler does not interleave with the sweep (fused, the kernel spills)
+  // Hessian-factor route (a.Wo set): the block arrives compensated by the
+  // updates through F = R U_BB above the diagonal blocks, is swept on U_BB
+  // like the inverse route, and hands on the error w^_j - o_j
   const bool hroute = kH && a.Wo != nullptr;
   auto load_w = [&](int64_t r0) {
     const int64_t rowc = min(r0 + grp, a.rows - 1);
@@ -299,55 +299,6 @@ __device__ __forceinline__ void sweep_block(const SweepArgs &a, const int i1, co
     const bool rv = row < a.rows;  // whole row group is valid or not
     const int64_t rowc = rv ? row : a.rows - 1;
     float *wrow = a.W + rowc * ld + i1;
-
-    if (hroute) {
-      // Hessian-factor route.  The loaded weights are y_k = o_k + sum_{i<k}
-      // (o_i - w^_i) T_ik over the columns before the block: exact for the
-      // block's first column, but the grid of a group is chosen from the
-      // compensated weights of all its columns with the earlier columns
-      // fixed, c = o + z U_BB with z_j = (y_j - o_j) R_jj (R_jj = 1 / U_jj,
-      // U_BB the inverse factor's diagonal block).  The block is then swept
-      // from c by the inverse-factor rule inside the block.
-      const f32x4_t d0 = *reinterpret_cast<const f32x4_t *>(Uinv + c0);
-      const f32x4_t d1 = *reinterpret_cast<const f32x4_t *>(Uinv + c0 + 4);
-      float zl[kCPL], cv[kCPL];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        zl[y] = (w[y] - o[y]) * d0[y];
-        zl[4 + y] = (w[4 + y] - o[4 + y]) * d1[y];
-      }
-#pragma unroll
-      for (int y = 0; y < kCPL; ++y) cv[y] = o[y];
-      // rows j of U_BB read two steps ahead (rows past B are zero in LDS),
-      // as in the column steps below
-      f32x4_t qa0 = *reinterpret_cast<const f32x4_t *>(Ub + c0);
-      f32x4_t qa1 = *reinterpret_cast<const f32x4_t *>(Ub + c0 + 4);
-      f32x4_t qb0 = *reinterpret_cast<const f32x4_t *>(Ub + kMaxB + c0);
-      f32x4_t qb1 = *reinterpret_cast<const f32x4_t *>(Ub + kMaxB + c0 + 4);
-      __builtin_amdgcn_sched_barrier(0);
-      static_for<0, kMaxB / kCPL>([&](auto ow) {
-        constexpr int kOw = decltype(ow)::value;
-        static_for<0, kCPL>([&](auto xs) {
-          constexpr int x = decltype(xs)::value;
-          constexpr int j = kOw * kCPL + x;
-          const f32x4_t u0 = qa0, u1 = qa1;
-          qa0 = qb0;
-          qa1 = qb1;
-          qb0 = *reinterpret_cast<const f32x4_t *>(Ub + (j + 2) * kMaxB + c0);
-          qb1 = *reinterpret_cast<const f32x4_t *>(Ub + (j + 2) * kMaxB + c0 + 4);
-          __builtin_amdgcn_sched_barrier(0);
-          const float zj = row_bcast<kOw>(zl[x]);
-#pragma unroll
-          for (int yy = 0; yy < 4; ++yy) {
-            cv[yy] = fmaf(zj, u0[yy], cv[yy]);
-            cv[4 + yy] = fmaf(zj, u1[yy], cv[4 + yy]);
-          }
-        });
-      });
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int y = 0; y < kCPL; ++y) w[y] = cv[y];
-    }
 
     // grid state of the current group (per row group, identical in its lanes)
     float s = 1.f, rs = 1.f, z = 0.f;       // affine

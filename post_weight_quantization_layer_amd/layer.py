@@ -35,12 +35,13 @@ def fast_route(rows: int, cols: int, *, group: int, block: int, grid: str = "aff
 
     The Hessian-factor route needs the affine grid, block 128, a group that
     divides 128 and cols a multiple of 128.  It saves the triangular inverse,
-    about d^3/3 products, and costs each block's conversion in the sweep,
-    about rows * d * 128 FMAs on the VALU.  Measured on MI355X the two break
-    even near rows = 2.5e-4 d^2 (4096 x 11008: 27.4 against 29.9 ms per
-    layer; 28672 x 8192: 28.5 against 26.5 ms)."""
+    about d^3/3 products, for d^2 * 128 products that scale R's block columns
+    by U's diagonal blocks and a read of the uncompensated weights in the
+    sweep; ``rows`` is kept for the choice, which no layer shape measured so
+    far has needed."""
+    del rows
     ok = grid == "affine" and block == 128 and 128 % group == 0 and cols % 128 == 0
-    return "hessian" if ok and rows <= 2.5e-4 * cols * cols else "inverse"
+    return "hessian" if ok else "inverse"
 
 
 class GptqLayer:

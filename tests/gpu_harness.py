@@ -52,13 +52,20 @@ class GpuOut:
 def expected_factor(U: np.ndarray, H: np.ndarray, diag: np.ndarray, perm: np.ndarray,
                     percdamp: float, route: str) -> np.ndarray:
     """What gptq_prepare_hinv writes for a route, from the oracle: U itself
-    (inverse route), or U inside the 128 x 128 diagonal blocks and the unit
-    factor T of the damped Hessian above them (Hessian route)."""
+    (inverse route), or U inside the 128 x 128 diagonal blocks and, above
+    each diagonal block B, R_{<B,B} U_BB with Hp = R R^T (Hessian route;
+    R = T diag(R) from the oracle's unit factor T, diag(R) = 1 / diag(U))."""
     if route == "inverse":
         return U
     T = O.unit_upper_factor(O.damped_processing_hessian(H, diag, perm, percdamp))
-    b = np.arange(U.shape[0]) // 128
-    return np.where(b[:, None] == b[None, :], U, T)
+    T /= np.diag(U)[None, :]          # R, in place
+    d = U.shape[0]
+    F = np.zeros_like(U)
+    for b0 in range(0, d, 128):
+        b1 = min(b0 + 128, d)
+        F[b0:b1, b0:b1] = U[b0:b1, b0:b1]
+        F[:b0, b0:b1] = T[:b0, b0:b1] @ U[b0:b1, b0:b1]
+    return F
 
 
 def gpu_layer(cfg: I.LayerConfig, W: np.ndarray, chunks, dev="cuda", keep_H=True,

@@ -1,20 +1,19 @@
 """The compensation carried by the Hessian's own factor (CPU, float64).
 
-The HIP path can take the compensation between blocks from T, the unit upper
-factor with Hp = T D T^T, instead of U, the Cholesky factor of Hp^-1
-("GPTQ", section Komponenty).  With R = U^-1 (so T = R diag(R)^-1) the
+The HIP path can take the compensation between blocks from the factor of
+the damped Hessian itself instead of U, the Cholesky factor of Hp^-1
+("GPTQ", section Komponenty).  With Hp = R R^T (R upper, so U = R^-1), the
 pages' errors satisfy W - W^ = E U, hence E = (W - W^) R.  Writing o for the
-weights before any compensation, the weight a column k has when its turn
-comes is
+weights before any compensation, the compensated weights of a block B at its
+turn, with every earlier column fixed, are
 
-    w_k = o_k + sum_{j<k} (o_j - w^_j) T_jk,
+    c_B = o_B + (o - w^)_{<B} R_{<B,B} U_BB,
 
-so between blocks the later columns take y -= (w^_j - o_j) T_jk.  Inside a
-block a group's grid is chosen from the compensated weights of all its
-columns with the earlier columns fixed -- for the block B starting at i1,
-c = o_B + z U_BB with z_j = (y_j - o_j) R_jj -- and the pages' rule then runs
-on U_BB, the inverse factor's diagonal block, from c.  Only U's diagonal
-blocks are needed, which a blocked Cholesky forms anyway.
+U_BB being U's diagonal block of B (the inverse of R's).  So the lazy
+updates can hand each block its compensated weights directly through
+M = R_{<B,B} U_BB, with the error w^_j - o_j, and the pages' rule runs
+inside the block on U_BB.  Only U's diagonal blocks are inverted, which a
+blocked Cholesky forms anyway; no inverse of the whole factor is needed.
 
 This file checks that formulation in float64 against the oracle, which
 follows the pages' route: the same codes (decisions in float32 on both
@@ -26,42 +25,52 @@ import pytest
 import oracle as O
 
 
-def sweep_hessian_factor(Wp, U, T, spec, block):
-    """Blocked sweep over Wp (processing order): T between blocks, U's
-    diagonal blocks inside them."""
+def hessian_route_factor(U, T, block):
+    """F: U's diagonal blocks, and M = R_{<B,B} U_BB above them (R = T diag(R),
+    diag(R) = 1 / diag(U)); zero below."""
+    d = U.shape[0]
+    R = T / np.diag(U)[None, :]
+    F = np.zeros((d, d))
+    for b0 in range(0, d, block):
+        b1 = min(b0 + block, d)
+        F[b0:b1, b0:b1] = U[b0:b1, b0:b1]
+        F[:b0, b0:b1] = R[:b0, b0:b1] @ U[b0:b1, b0:b1]
+    return F
+
+
+def sweep_hessian_factor(Wp, F, spec, block):
+    """Blocked sweep over Wp (processing order): between blocks the updates
+    go through F's blocks above the diagonal with the error w^ - o; inside a
+    block the pages' rule runs on F's diagonal block (U_BB)."""
     o = np.array(Wp, dtype=np.float64)
-    Y = o.copy()
-    r, d = Y.shape
+    W = o.copy()
+    r, d = W.shape
     Q = np.zeros((r, d))
     What = np.zeros((r, d))
     span = spec.span
-    Rd = 1.0 / np.diag(U)          # R_jj
     for i1 in range(0, d, block):
         i2 = min(i1 + block, d)
-        Ub = U[i1:i2, i1:i2]
-        z = (Y[:, i1:i2] - o[:, i1:i2]) * Rd[None, i1:i2]
-        C = o[:, i1:i2] + z @ Ub
         E = np.zeros((r, i2 - i1))
         for j in range(i1, i2):
-            jj = j - i1
             if j % span == 0:
-                v = C[:, jj:jj + span].astype(np.float32)
+                v = W[:, j:j + span].astype(np.float32)
                 if spec.grid == "affine":
                     s, zp, _ = O.affine_params(v, spec.bits)
                 else:
                     _, _, _, _, S, M = O.q4k_params(v, spec.bits)
             if spec.grid == "affine":
-                q, wq = O.affine_quantize(C[:, jj].astype(np.float32), s, zp, spec.bits)
+                q, wq = O.affine_quantize(W[:, j].astype(np.float32), s, zp, spec.bits)
             else:
                 b = (j % span) // O.Q4K_SUB
-                q, wq = O.q4k_quantize(C[:, jj].astype(np.float32), S[:, b], M[:, b], spec.bits)
+                q, wq = O.q4k_quantize(W[:, j].astype(np.float32), S[:, b], M[:, b], spec.bits)
             wq = wq.astype(np.float64)
-            e = (C[:, jj] - wq) / Ub[jj, jj]
-            C[:, jj + 1:] -= np.outer(e, Ub[jj, jj + 1:])
-            E[:, jj] = wq - o[:, j]
+            e = (W[:, j] - wq) / F[j, j]
+            W[:, j + 1:i2] -= np.outer(e, F[j, j + 1:i2])
+            E[:, j - i1] = wq - o[:, j]
             Q[:, j], What[:, j] = q, wq
+            W[:, j] = wq
         if i2 < d:
-            Y[:, i2:] -= E @ T[i1:i2, i2:]
+            W[:, i2:] -= E @ F[i1:i2, i2:]
     return Q, What
 
 
@@ -83,9 +92,9 @@ def test_unit_factor_sweep_equals_oracle(grid, bits, group, block, act):
     res = O.quantize_layer(W, H, diag, bits=bits, group=group, block=None,
                            act_order=act, percdamp=0.01, grid=grid)
     Hp = O.damped_processing_hessian(H, diag, res.perm, 0.01)
-    T = O.unit_upper_factor(Hp)
+    F = hessian_route_factor(res.U, O.unit_upper_factor(Hp), block)
     spec = O.GridSpec(grid, bits, group)
-    Q, What = sweep_hessian_factor(W[:, res.perm], res.U, T, spec, block)
+    Q, What = sweep_hessian_factor(W[:, res.perm], F, spec, block)
     np.testing.assert_array_equal(Q, res.sweep.q)
     np.testing.assert_allclose(What, res.sweep.what, rtol=0, atol=1e-7)
 
@@ -104,7 +113,7 @@ def test_unit_factor_dead_column():
     Hp = O.damped_processing_hessian(H, diag, res.perm, 0.01)
     Wd = W.copy()
     Wd[:, res.dead] = 0.0
-    Q, What = sweep_hessian_factor(Wd[:, res.perm], res.U, O.unit_upper_factor(Hp),
-                                   O.GridSpec("affine", 4, 16), 16)
+    F = hessian_route_factor(res.U, O.unit_upper_factor(Hp), 16)
+    Q, What = sweep_hessian_factor(Wd[:, res.perm], F, O.GridSpec("affine", 4, 16), 16)
     np.testing.assert_array_equal(Q, res.sweep.q)
     np.testing.assert_allclose(What, res.sweep.what, rtol=0, atol=1e-7)
