@@ -157,9 +157,13 @@ def test_hessian_route_parity(name):
     assert err <= 1e-4
     rep = classify_codes(g.q[:, o.perm], o.sweep, cfg.grid, cfg.group)
     log(f"[parity] {name} hessian route codes: {rep.mismatches}/{rep.n} differ in "
-        f"{rep.rows_with_mismatch} rows")
-    assert_codes(rep)
+        f"{rep.rows_with_mismatch} rows, at most {rep.max_step} steps")
+    # every GPU decision is the oracle's or the other side of a tie of the
+    # oracle's, with the tie's cascade replayed exactly
     check_replay(cfg, W, o, g, tag=f"{name} hessian route")
+    # a tie's cascade carries the other choice forward through the
+    # compensation, which can move a later code of that row by two steps
+    assert_codes(rep, max_step=2)
     np.testing.assert_array_equal(g.g_idx, o.g_idx)
     e_gpu = O.reconstruction_error(W, g.W_hat, H)
     e_or = O.reconstruction_error(W, o.what, H)
