@@ -508,7 +508,7 @@ __device__ __forceinline__ void sweep_block(const SweepArgs &a, const int i1, co
       uint8_t *qrow = a.q + row * ld + i1;
       float *erow = Err + row * a.ldE;
       // Hessian-factor route: the later columns take the error against the
-      // uncompensated weight, w^_j - o_j, through T
+      // uncompensated weight, w^_j - o_j, through R_{<B,B} U_BB
       if (hroute) {
 #pragma unroll
         for (int x = 0; x < kCPL; ++x) et[x] = wt[x] - o[x];

@@ -47,7 +47,8 @@ class GptqLayer:
     """Buffers and call order for quantizing one layer on the current device.
 
     ``route``: "inverse" (U, the Cholesky factor of the inverse Hessian),
-    "hessian" (the Hessian's own unit factor between 128-column blocks) or
+    "hessian" (the Hessian's own Cholesky factor times U's diagonal blocks
+    between 128-column blocks) or
     "auto" (fast_route)."""
 
     def __init__(self, rows: int, cols: int, *, bits: int, group: int, block: int,
